@@ -1,0 +1,343 @@
+// Host side of the C ABI in include/flh.h: argument validation, workspace
+// carve-up and the launch sequence of each call.  No device memory is allocated
+// here and nothing waits on the device; every check happens before the first
+// launch, so a rejected call enqueues nothing.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <vector>
+
+#include "flh.h"
+#include "flh_internal.h"
+
+using namespace flh;
+
+namespace {
+
+constexpr int32_t kDefaultSplit = 16384;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // token/vocabulary indices are int32 on device
+
+enum KernelId : int32_t {
+  kIdSpans = 0,
+  kIdFwdGemm,
+  kIdFwdCombine,
+  kIdBwdLists,
+  kIdDlogits,
+  kIdDhidden,
+  kIdDweight,
+  kIdFinalize,
+  kIdCount
+};
+const char *const kKernelNames[kIdCount] = {
+    "spans_build", "fwd_logits_softmax", "fwd_combine", "bwd_lists",
+    "dlogits",     "dhidden_spans",      "dweight",     "dhidden_finalize"};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+int64_t elt_size(flh_dtype dt) { return dt == FLH_BF16 ? 2 : 4; }
+bool dtype_ok(flh_dtype dt) { return dt == FLH_BF16 || dt == FLH_F32; }
+
+// Sizes shared by both calls: T, V in [1, 2^31); H a positive multiple of one
+// 16-byte chunk.
+bool dims_ok(flh_dtype dt, int64_t T, int64_t H, int64_t V) {
+  const int64_t per = 16 / elt_size(dt);
+  return T > 0 && T < kMaxDim && V > 0 && V < kMaxDim && H > 0 && H < kMaxDim && H % per == 0;
+}
+
+int32_t split_or_default(int32_t s) { return s == 0 ? kDefaultSplit : s; }
+
+size_t fwd_bytes(int64_t T, int64_t V) { return (size_t)cdiv(V, kTile) * (size_t)T * 16; }
+
+struct BwdLayout {
+  size_t counts, tile_list, span_tiles, D, acc, total;
+  int64_t span_tile_cap;
+};
+
+// Backward workspace: [counts | token-tile list | span-tile list | d-logits
+// staging sized by the widest live split | fp32 dH accumulator].
+BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
+  BwdLayout L{};
+  const int64_t per = 16 / elt_size(dt);
+  const int64_t n_skip = cdiv(T, kSkipTile);
+  // every span holds >= 1 token and spans are >= 1 token apart: <= ceil(T/2) spans
+  L.span_tile_cap = cdiv(T, kSpanTile) + (T + 1) / 2 + 1;
+  const int64_t w_max = V < S ? V : S;
+  const int64_t ld_max = cdiv(w_max, per) * per;
+  size_t off = 0;
+  L.counts = off;
+  off = align_up(off + 64, 256);
+  L.tile_list = off;
+  off = align_up(off + (size_t)n_skip * 4, 256);
+  L.span_tiles = off;
+  off = align_up(off + (size_t)L.span_tile_cap * 8, 256);
+  L.D = off;
+  off = align_up(off + (size_t)T * (size_t)ld_max * (size_t)elt_size(dt), 256);
+  L.acc = off;
+  off = align_up(off + (size_t)T * (size_t)H * 4, 256);
+  L.total = off;
+  return L;
+}
+
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int grid_for(int64_t upper_items, int cus) {
+  int64_t g = upper_items < cus ? upper_items : cus;
+  return g < 1 ? 1 : (int)g;
+}
+
+// ---- launch tracing (per host thread) ----
+struct Trace {
+  bool on = false;
+  int32_t cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<int32_t> kid, split;
+};
+Trace &trace() {
+  thread_local Trace tr;
+  return tr;
+}
+
+template <class F>
+flh_status run(int32_t kid, int32_t split, hipStream_t st, F &&f) {
+  Trace &tr = trace();
+  const bool rec = tr.on && tr.n < tr.cap;
+  if (rec && hipEventRecord(tr.ev[2 * tr.n], st) != hipSuccess) return FLH_E_HIP;
+  if (f() != hipSuccess) return FLH_E_HIP;
+  if (rec) {
+    if (hipEventRecord(tr.ev[2 * tr.n + 1], st) != hipSuccess) return FLH_E_HIP;
+    tr.kid[tr.n] = kid;
+    tr.split[tr.n] = split;
+    ++tr.n;
+  }
+  return FLH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t flh_abi_version(void) { return FLH_ABI_VERSION; }
+
+const char *flh_status_string(flh_status s) {
+  switch (s) {
+    case FLH_OK: return "ok";
+    case FLH_E_NULL: return "a required pointer is NULL";
+    case FLH_E_SHAPE: return "invalid size";
+    case FLH_E_DTYPE: return "unknown dtype";
+    case FLH_E_ALIGN: return "misaligned pointer";
+    case FLH_E_WORKSPACE: return "workspace too small";
+    case FLH_E_META: return "active metadata inconsistent with the call";
+    case FLH_E_UNSUPPORTED: return "unsupported request";
+    case FLH_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t flh_tile_m(flh_dtype dt) { return dtype_ok(dt) ? kSkipTile : 0; }
+
+int64_t flh_span_capacity(int64_t T, int32_t max_gap) {
+  if (T <= 0 || max_gap < 0) return 0;
+  return (T + (int64_t)max_gap + 1) / ((int64_t)max_gap + 2);
+}
+
+size_t flh_workspace_bytes(flh_op op, flh_dtype dt, int64_t T, int64_t H, int64_t V,
+                           int32_t vocab_split) {
+  if (!dtype_ok(dt)) return 0;
+  switch (op) {
+    case FLH_OP_SPANS: return 0;
+    case FLH_OP_FORWARD: return dims_ok(dt, T, H, V) ? fwd_bytes(T, V) : 0;
+    case FLH_OP_BACKWARD: {
+      const int32_t S = split_or_default(vocab_split);
+      if (!dims_ok(dt, T, H, V) || S <= 0 || S % kTile != 0) return 0;
+      return bwd_layout(dt, T, H, V, S).total;
+    }
+  }
+  return 0;
+}
+
+flh_status flh_spans_build(const uint8_t *loss_mask, flh_active_meta *meta, void *ws,
+                           size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!loss_mask || !meta) return FLH_E_NULL;
+  if (!meta->spans || !meta->num_spans || !meta->tile_bits || !meta->active_count) return FLH_E_NULL;
+  if (meta->T <= 0 || meta->T >= kMaxDim || meta->tile_m <= 0) return FLH_E_SHAPE;
+  if (meta->max_gap < 0) return FLH_E_META;
+  if (meta->span_cap < flh_span_capacity(meta->T, meta->max_gap)) return FLH_E_META;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return run(kIdSpans, -1, st, [&] {
+    return launch_spans(loss_mask, meta->T, meta->max_gap, meta->tile_m, meta->span_cap,
+                        meta->spans, meta->num_spans, meta->tile_bits, meta->active_count, st);
+  });
+}
+
+flh_status flh_forward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                       int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
+                       void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dt)) return FLH_E_DTYPE;
+  if (!h || !W || !targets || !logprob || !entropy || !lse || !ws) return FLH_E_NULL;
+  if (!dims_ok(dt, T, H, V)) return FLH_E_SHAPE;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(ws, 256)) return FLH_E_ALIGN;
+  if (ws_bytes < fwd_bytes(T, V)) return FLH_E_WORKSPACE;
+  const int cus = num_cus();
+  if (cus <= 0) return FLH_E_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  GemmArgs a{};
+  a.T = T;
+  a.H = H;
+  a.V = V;
+  a.h = h;
+  a.W = W;
+  a.targets = targets;
+  a.part = reinterpret_cast<float *>(ws);
+  const int grid = grid_for(cdiv(V, kTile) * cdiv(T, kTile), cus);
+  flh_status s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwd, a, grid, st); });
+  if (s != FLH_OK) return s;
+  return run(kIdFwdCombine, -1, st, [&] {
+    return launch_combine(T, V, a.part, targets, logprob, entropy, lse, st);
+  });
+}
+
+flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                        const float *lse, const float *entropy, const float *grad_logprob,
+                        const float *grad_entropy, const uint8_t *loss_mask,
+                        const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
+                        int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
+                        size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dt)) return FLH_E_DTYPE;
+  if (!h || !W || !targets || !lse || !entropy || !d_hidden || !d_weight || !ws) return FLH_E_NULL;
+  const int32_t S = split_or_default(vocab_split);
+  if (!dims_ok(dt, T, H, V) || S <= 0 || S % kTile != 0) return FLH_E_SHAPE;
+  if (meta) {
+    if (!loss_mask) return FLH_E_META;
+    if (!meta->spans || !meta->num_spans || !meta->tile_bits) return FLH_E_NULL;
+    if (meta->T != T || meta->tile_m != flh_tile_m(dt) || meta->span_cap < 0) return FLH_E_META;
+  }
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(d_hidden, 16) || !aligned(d_weight, 16) ||
+      !aligned(ws, 256))
+    return FLH_E_ALIGN;
+  const BwdLayout L = bwd_layout(dt, T, H, V, S);
+  if (ws_bytes < L.total) return FLH_E_WORKSPACE;
+  const int cus = num_cus();
+  if (cus <= 0) return FLH_E_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char *base = reinterpret_cast<char *>(ws);
+  const int64_t per = 16 / elt_size(dt);
+
+  GemmArgs a{};
+  a.T = T;
+  a.H = H;
+  a.V = V;
+  a.h = h;
+  a.W = W;
+  a.targets = targets;
+  a.lse = lse;
+  a.entropy = entropy;
+  a.grad_lp = grad_logprob;
+  a.grad_ent = grad_entropy;
+  a.mask = loss_mask;
+  a.counts = reinterpret_cast<int32_t *>(base + L.counts);
+  a.tile_list = reinterpret_cast<int32_t *>(base + L.tile_list);
+  a.span_tiles = reinterpret_cast<int32_t *>(base + L.span_tiles);
+  a.n_skip_tiles = (int32_t)cdiv(T, kSkipTile);
+  a.D = base + L.D;
+  a.dh_acc = reinterpret_cast<float *>(base + L.acc);
+  a.dW = d_weight;
+
+  flh_status s = run(kIdBwdLists, -1, st, [&] {
+    return launch_lists(T, meta ? meta->tile_bits : nullptr, meta ? meta->spans : nullptr,
+                        meta ? meta->num_spans : nullptr, meta ? meta->span_cap : 0,
+                        reinterpret_cast<int32_t *>(base + L.tile_list),
+                        reinterpret_cast<int32_t *>(base + L.counts),
+                        reinterpret_cast<int32_t *>(base + L.span_tiles), L.span_tile_cap, st);
+  });
+  if (s != FLH_OK) return s;
+
+  const int64_t n_splits = cdiv(V, S);
+  const int64_t h_tiles = cdiv(H, kTile);
+  for (int64_t sp = 0; sp < n_splits; ++sp) {
+    // live width of this split: the staging row stride and every grid below
+    // come from it, never from S.
+    const int64_t Ws = (V - sp * S) < S ? (V - sp * S) : S;
+    a.v_base = sp * S;
+    a.Ws = (int32_t)Ws;
+    a.ld_d = (int32_t)(cdiv(Ws, per) * per);
+    a.first_split = sp == 0;
+    const int32_t tag = (int32_t)sp;
+    const int64_t v_tiles = cdiv(a.ld_d, kTile);
+    s = run(kIdDlogits, tag, st, [&] {
+      return launch_gemm((int)dt, kDlogits, a, grid_for(v_tiles * cdiv(a.n_skip_tiles, 2), cus), st);
+    });
+    if (s != FLH_OK) return s;
+    s = run(kIdDhidden, tag, st, [&] {
+      return launch_gemm((int)dt, kDhidden, a, grid_for(L.span_tile_cap * h_tiles, cus), st);
+    });
+    if (s != FLH_OK) return s;
+    s = run(kIdDweight, tag, st, [&] {
+      return launch_gemm((int)dt, kDweight, a, grid_for(cdiv(Ws, kTile) * h_tiles, cus), st);
+    });
+    if (s != FLH_OK) return s;
+  }
+  return run(kIdFinalize, -1, st, [&] {
+    return launch_finalize((int)dt, T, H, a.dh_acc, loss_mask, d_hidden, st);
+  });
+}
+
+flh_status flh_trace_begin(int32_t capacity) {
+  Trace &tr = trace();
+  if (tr.on || capacity <= 0) return FLH_E_UNSUPPORTED;
+  tr.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto &e : tr.ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto &x : tr.ev)
+        if (x) hipEventDestroy(x);
+      tr.ev.clear();
+      return FLH_E_HIP;
+    }
+  tr.kid.assign(capacity, -1);
+  tr.split.assign(capacity, -1);
+  tr.cap = capacity;
+  tr.n = 0;
+  tr.on = true;
+  return FLH_OK;
+}
+
+int32_t flh_trace_end(flh_trace_record *records, int32_t max_records) {
+  Trace &tr = trace();
+  if (!tr.on) return -1;
+  int32_t n = tr.n;
+  bool err = false;
+  for (int32_t i = 0; i < n; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(tr.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, tr.ev[2 * i], tr.ev[2 * i + 1]) != hipSuccess)
+      err = true;
+    if (records && i < max_records) records[i] = flh_trace_record{tr.kid[i], tr.split[i], ms};
+  }
+  for (auto &e : tr.ev) hipEventDestroy(e);
+  tr.ev.clear();
+  tr.on = false;
+  tr.n = 0;
+  return err ? -1 : n;
+}
+
+const char *flh_kernel_name(int32_t kernel_id) {
+  return (kernel_id >= 0 && kernel_id < kIdCount) ? kKernelNames[kernel_id] : "unknown";
+}
+
+}  // extern "C"

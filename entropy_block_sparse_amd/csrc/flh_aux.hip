@@ -1,0 +1,339 @@
+// Small, memory-bound kernels around the contractions:
+//
+//   spans    loss mask -> tile bitmap, ordered active spans, span count, active
+//            count (SkyRL #2376, "How it works": one builder derives the forward
+//            active mask and the backward spans; Bugbot "Overview": runs of the
+//            RL loss mask coalesced across gaps <= 128).  Built on the device.
+//   lists    bitmap + spans -> the backward's work lists: token tiles (active
+//            ones first, so d-logits workgroups pair up active tiles) and
+//            span-local row tiles for the hidden-gradient projection.
+//   combine  per-tile softmax states -> logprob, entropy, lse per token.
+//   finalize fp32 hidden-gradient accumulator -> output dtype, inactive rows +0.
+//
+// spans and lists run as one workgroup of 1024 threads: the mask is at most a
+// few hundred KiB, so a single pass through L2 is far cheaper than a multi-kernel
+// scan, and nothing has to be synchronised with the host.
+#include <hip/hip_runtime.h>
+
+#include "flh_internal.h"
+
+namespace flh {
+namespace {
+
+constexpr int kBlock = 1024;
+
+// Inclusive scans over the 1024 threads of the block (Hillis-Steele in LDS).
+template <typename V, typename Op>
+__device__ V block_scan(V v, V *sh, Op op) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kBlock; off <<= 1) {
+    V x = v;
+    if (tid >= off) x = op(sh[tid - off], v);
+    __syncthreads();
+    v = x;
+    sh[tid] = v;
+    __syncthreads();
+  }
+  return v;
+}
+
+struct AddOp {
+  __device__ int64_t operator()(int64_t a, int64_t b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; }
+};
+
+__global__ __launch_bounds__(kBlock) void spans_kernel(const uint8_t *__restrict__ mask, int64_t T,
+                                                       int32_t G, int32_t tile_m, int64_t cap,
+                                                       int32_t *__restrict__ spans,
+                                                       int32_t *__restrict__ num_spans,
+                                                       uint32_t *__restrict__ bits,
+                                                       int32_t *__restrict__ active_count) {
+  __shared__ int64_t sh[kBlock];
+  const int tid = threadIdx.x;
+  const int64_t chunk = (T + kBlock - 1) / kBlock;
+  const int64_t c0 = (tid * chunk < T) ? tid * chunk : T;
+  const int64_t c1 = (c0 + chunk < T) ? c0 + chunk : T;
+
+  // pass 1: active count, first and last active token of the chunk
+  int64_t cnt = 0, first = -1, last = -1;
+  for (int64_t t = c0; t < c1; ++t) {
+    if (mask[t]) {
+      ++cnt;
+      if (first < 0) first = t;
+      last = t;
+    }
+  }
+  block_scan(cnt, sh, AddOp());
+  const int64_t A = sh[kBlock - 1];
+  __syncthreads();
+  // last active token before this chunk (-1 if none): exclusive max-scan of `last`
+  block_scan(last, sh, MaxOp());
+  const int64_t prev = (tid > 0) ? sh[tid - 1] : -1;
+  __syncthreads();
+  // first active token after this chunk (-1 if none): a max-scan of -first over
+  // the threads in reverse order (position p holds thread kBlock-1-p); "no active
+  // token" is INT64_MIN, neutral for max.
+  sh[kBlock - 1 - tid] = (first >= 0) ? -first : INT64_MIN;
+  __syncthreads();
+  const int64_t rkey = sh[tid];
+  __syncthreads();
+  block_scan(rkey, sh, MaxOp());
+  // sh[p] = max of -first over threads >= kBlock-1-p; threads after tid end at
+  // position kBlock-2-tid.
+  const int64_t after_pos = kBlock - 2 - tid;
+  const int64_t after_key = (after_pos >= 0) ? sh[after_pos] : INT64_MIN;
+  const int64_t next = (after_key == INT64_MIN) ? -1 : -after_key;
+  __syncthreads();
+
+  // pass 2: span starts in this chunk
+  int64_t starts = 0;
+  {
+    int64_t pv = prev;
+    for (int64_t t = c0; t < c1; ++t) {
+      if (mask[t]) {
+        if (pv < 0 || t - pv - 1 > (int64_t)G) ++starts;
+        pv = t;
+      }
+    }
+  }
+  const int64_t st_incl = block_scan(starts, sh, AddOp());
+  const int64_t total = sh[kBlock - 1];
+  __syncthreads();
+  int64_t k = st_incl - starts;  // global index of the next span to start
+
+  // pass 3: emit starts and ends
+  {
+    int64_t pv = prev;
+    for (int64_t t = c0; t < c1; ++t) {
+      if (mask[t]) {
+        if (pv < 0 || t - pv - 1 > (int64_t)G) {
+          if (pv >= c0 && k - 1 < cap) spans[2 * (k - 1) + 1] = (int32_t)(pv + 1);
+          if (k < cap) spans[2 * k] = (int32_t)t;
+          ++k;
+        }
+        pv = t;
+      }
+    }
+    if (last >= 0 && (next < 0 || next - last - 1 > (int64_t)G)) {
+      if (k - 1 < cap) spans[2 * (k - 1) + 1] = (int32_t)(last + 1);
+    }
+  }
+
+  // tile bitmap: one wave covers 64 consecutive tiles -> two words
+  const int64_t n_tiles = (T + tile_m - 1) / tile_m;
+  const int64_t n_words = (n_tiles + 31) / 32;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int64_t base = 0; base < n_tiles; base += kBlock) {
+    const int64_t tile = base + wave * 64 + lane;
+    int flag = 0;
+    if (tile < n_tiles) {
+      const int64_t t0 = tile * tile_m;
+      const int64_t t1 = (t0 + tile_m < T) ? t0 + tile_m : T;
+      for (int64_t t = t0; t < t1 && !flag; ++t) flag = mask[t] != 0;
+    }
+    const uint64_t ballot = __ballot(flag);
+    const int64_t w0 = (base + wave * 64) / 32;
+    if (lane == 0 && w0 < n_words) bits[w0] = (uint32_t)(ballot & 0xffffffffu);
+    if (lane == 0 && w0 + 1 < n_words) bits[w0 + 1] = (uint32_t)(ballot >> 32);
+  }
+
+  if (tid == 0) {
+    *num_spans = (int32_t)total;
+    *active_count = (int32_t)A;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t *__restrict__ bits,
+                                                       const int32_t *__restrict__ spans,
+                                                       const int32_t *__restrict__ num_spans,
+                                                       int64_t span_cap, int32_t *__restrict__ tile_list,
+                                                       int32_t *__restrict__ counts,
+                                                       int32_t *__restrict__ span_tiles,
+                                                       int64_t span_tile_cap) {
+  __shared__ int64_t sh[kBlock];
+  const int tid = threadIdx.x;
+  const int64_t n_tiles = (T + kSkipTile - 1) / kSkipTile;
+  auto active = [&](int64_t i) -> int64_t {
+    return bits ? (int64_t)((bits[i >> 5] >> (i & 31)) & 1u) : 1;
+  };
+
+  // number of active token tiles
+  int64_t c = 0;
+  for (int64_t i = tid; i < n_tiles; i += kBlock) c += active(i);
+  block_scan(c, sh, AddOp());
+  const int64_t n_act = sh[kBlock - 1];
+  __syncthreads();
+
+  // stable partition: active tiles ascending, then inactive tiles ascending
+  int64_t run_a = 0, run_i = 0;
+  for (int64_t base = 0; base < n_tiles; base += kBlock) {
+    const int64_t i = base + tid;
+    const int64_t valid = i < n_tiles ? 1 : 0;
+    const int64_t f = valid ? active(i) : 0;
+    const int64_t nf = valid - f;
+    const int64_t pa = block_scan(f, sh, AddOp());
+    const int64_t tot_a = sh[kBlock - 1];
+    __syncthreads();
+    const int64_t pi = block_scan(nf, sh, AddOp());
+    const int64_t tot_i = sh[kBlock - 1];
+    __syncthreads();
+    if (valid) {
+      if (f) tile_list[run_a + pa - 1] = (int32_t)i;
+      else tile_list[n_act + run_i + pi - 1] = (int32_t)i;
+    }
+    run_a += tot_a;
+    run_i += tot_i;
+  }
+
+  // span-local row tiles of at most kSpanTile rows, starting at each span start
+  int64_t ns = spans ? (int64_t)(*num_spans) : 1;
+  if (spans && ns > span_cap) ns = span_cap;
+  int64_t run = 0;
+  for (int64_t base = 0; base < ns; base += kBlock) {
+    const int64_t k = base + tid;
+    int64_t s = 0, e = 0;
+    if (k < ns) {
+      if (spans) {
+        s = spans[2 * k];
+        e = spans[2 * k + 1];
+      } else {
+        s = 0;
+        e = T;
+      }
+    }
+    const int64_t ntl = (e > s) ? (e - s + kSpanTile - 1) / kSpanTile : 0;
+    const int64_t incl = block_scan(ntl, sh, AddOp());
+    const int64_t tot = sh[kBlock - 1];
+    __syncthreads();
+    for (int64_t j = 0; j < ntl; ++j) {
+      const int64_t idx = run + incl - ntl + j;
+      if (idx < span_tile_cap) {
+        const int64_t r0 = s + j * kSpanTile;
+        span_tiles[2 * idx] = (int32_t)r0;
+        span_tiles[2 * idx + 1] = (int32_t)((r0 + kSpanTile < e) ? r0 + kSpanTile : e);
+      }
+    }
+    run += tot;
+  }
+  if (tid == 0) {
+    counts[0] = (int32_t)n_act;
+    counts[1] = (int32_t)(run < span_tile_cap ? run : span_tile_cap);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(int64_t T, int64_t V,
+                                                      const float4 *__restrict__ part,
+                                                      const int64_t *__restrict__ targets,
+                                                      float *__restrict__ logprob,
+                                                      float *__restrict__ entropy,
+                                                      float *__restrict__ lse) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const float ninf = -__builtin_huge_valf();
+  const int64_t n_vt = (V + kTile - 1) / kTile;
+  float M = ninf, s = 0.f, u = 0.f;
+  for (int64_t vt = 0; vt < n_vt; ++vt) {
+    const float4 p = part[vt * T + t];
+    const float Mn = fmaxf(M, p.x);
+    if (Mn == ninf) continue;
+    const bool e1 = (M == ninf), e2 = (p.x == ninf);
+    const float c1 = e1 ? 0.f : __expf(M - Mn);
+    const float c2 = e2 ? 0.f : __expf(p.x - Mn);
+    const float un = (e1 ? 0.f : c1 * (u + s * (M - Mn))) + (e2 ? 0.f : c2 * (p.z + p.y * (p.x - Mn)));
+    s = (e1 ? 0.f : s * c1) + (e2 ? 0.f : p.y * c2);
+    u = un;
+    M = Mn;
+  }
+  const int64_t y = targets[t];
+  const float ls = __logf(s);
+  const float l = M + ls;
+  float zy = __builtin_nanf("");
+  if (y >= 0 && y < V) zy = part[(y / kTile) * T + t].w;
+  lse[t] = l;
+  entropy[t] = ls - u / s;
+  logprob[t] = zy - l;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, const float *__restrict__ acc,
+                                                       const uint8_t *__restrict__ mask,
+                                                       T *__restrict__ dh) {
+  constexpr int kPer = 16 / sizeof(T);
+  const int64_t per_row = H / kPer;
+  const int64_t n = T_ * per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = idx / per_row;
+    const int64_t c = (idx - t * per_row) * kPer;
+    const bool act = mask ? (mask[t] != 0) : true;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (act) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(acc + t * H + c);
+        const float4 x1 = *reinterpret_cast<const float4 *>(acc + t * H + c + 4);
+        auto rne = [](float f) {
+          const uint32_t u = __float_as_uint(f);
+          return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        };
+        w[0] = rne(x0.x) | (rne(x0.y) << 16);
+        w[1] = rne(x0.z) | (rne(x0.w) << 16);
+        w[2] = rne(x1.x) | (rne(x1.y) << 16);
+        w[3] = rne(x1.z) | (rne(x1.w) << 16);
+      }
+      *reinterpret_cast<uint4 *>(dh + t * H + c) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (act) x = *reinterpret_cast<const float4 *>(acc + t * H + c);
+      *reinterpret_cast<float4 *>(dh + t * H + c) = x;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_spans(const uint8_t *mask, int64_t T, int32_t max_gap, int32_t tile_m,
+                        int64_t span_cap, int32_t *spans, int32_t *num_spans, uint32_t *tile_bits,
+                        int32_t *active_count, hipStream_t st) {
+  hipLaunchKernelGGL(spans_kernel, dim3(1), dim3(kBlock), 0, st, mask, T, max_gap, tile_m, span_cap,
+                     spans, num_spans, tile_bits, active_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spans,
+                        const int32_t *num_spans, int64_t span_cap, int32_t *tile_list,
+                        int32_t *counts, int32_t *span_tiles, int64_t span_tile_cap, hipStream_t st) {
+  hipLaunchKernelGGL(lists_kernel, dim3(1), dim3(kBlock), 0, st, T, tile_bits, spans, num_spans,
+                     span_cap, tile_list, counts, span_tiles, span_tile_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int64_t T, int64_t V, const float *part, const int64_t *targets,
+                          float *logprob, float *entropy, float *lse, hipStream_t st) {
+  const int64_t blocks = (T + 255) / 256;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, T, V,
+                     reinterpret_cast<const float4 *>(part), targets, logprob, entropy, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, const uint8_t *mask,
+                           void *dh, hipStream_t st) {
+  const int64_t per = dtype == 1 ? 8 : 4;
+  const int64_t n = T * (H / per);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  if (dtype == 1)
+    hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, T, H, acc,
+                       mask, reinterpret_cast<uint16_t *>(dh));
+  else
+    hipLaunchKernelGGL(finalize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, T, H, acc,
+                       mask, reinterpret_cast<float *>(dh));
+  return hipGetLastError();
+}
+
+}  // namespace flh

@@ -1,0 +1,73 @@
+// Internal interface between the host layer (flh_api.cpp) and the kernels.
+// Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace flh {
+
+// Macro tile of every contraction: 256 x 256 outputs per workgroup, 4 waves of
+// 128 x 128, K staged 128 bytes at a time (64 bf16 or 32 fp32).
+constexpr int kTile = 256;
+// Token-tile height of the d-logits skip bitmap; two such tiles form the token
+// side of one d-logits workgroup tile.
+constexpr int kSkipTile = 128;
+// Rows per span-local hidden-gradient tile.
+constexpr int kSpanTile = 256;
+
+enum GemmKind : int {
+  kFwd = 0,   // z = W h^T tile + online softmax partials          (K = H)
+  kDlogits,   // recompute z over active token tiles -> d-logits  (K = H)
+  kDhidden,   // dH[span rows] (+)= D[span rows, :] W_s           (K = W_s)
+  kDweight,   // dW[split rows] = D^T h                          (K = T)
+};
+
+// Everything a contraction kernel needs; plain data, passed by value.
+struct GemmArgs {
+  int64_t T, H, V;
+  // vocabulary split (d-logits, dH, dW)
+  int64_t v_base;          // first vocabulary row of the split
+  int32_t Ws;              // live width of the split
+  int32_t ld_d;            // row stride (elements) of the d-logits staging buffer
+  // inputs
+  const void *h;           // [T, H]
+  const void *W;           // [V, H]
+  const int64_t *targets;  // [T]
+  const float *lse;        // [T]
+  const float *entropy;    // [T]
+  const float *grad_lp;    // [T] or null
+  const float *grad_ent;   // [T] or null
+  const uint8_t *mask;     // [T] or null (all active)
+  // work lists (backward), device memory
+  const int32_t *tile_list;   // token tiles: active ones ascending, then inactive ascending
+  const int32_t *counts;      // [0] active token tiles, [1] span tiles
+  const int32_t *span_tiles;  // [n][2] half-open token rows
+  int32_t n_skip_tiles;       // ceil(T / kSkipTile)
+  // outputs / staging
+  float *part;             // forward partials [ceil(V/256)][T][4]
+  void *D;                 // d-logits staging [T][ld_d]
+  float *dh_acc;           // fp32 hidden-gradient accumulator [T][H]
+  int32_t first_split;     // dH: 1 -> overwrite, 0 -> accumulate
+  void *dW;                // [V][H]
+};
+
+// dtype: 0 = fp32, 1 = bf16 (flh_dtype values)
+hipError_t launch_gemm(int dtype, GemmKind kind, const GemmArgs &a, int grid, hipStream_t st);
+
+hipError_t launch_spans(const uint8_t *mask, int64_t T, int32_t max_gap, int32_t tile_m,
+                        int64_t span_cap, int32_t *spans, int32_t *num_spans,
+                        uint32_t *tile_bits, int32_t *active_count, hipStream_t st);
+
+hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spans,
+                        const int32_t *num_spans, int64_t span_cap, int32_t *tile_list,
+                        int32_t *counts, int32_t *span_tiles, int64_t span_tile_cap,
+                        hipStream_t st);
+
+hipError_t launch_combine(int64_t T, int64_t V, const float *part, const int64_t *targets,
+                          float *logprob, float *entropy, float *lse, hipStream_t st);
+
+hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc,
+                           const uint8_t *mask, void *dh, hipStream_t st);
+
+}  // namespace flh

@@ -1,0 +1,224 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Each function has the name of the C entry point it calls.  PyTorch supplies
+device memory (outputs, metadata arrays, workspace) and the current stream;
+every step of the computation runs in the HIP kernels of libflh.so.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import List, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import FLH_BF16, FLH_F32, OP_BACKWARD, OP_FORWARD, ActiveMeta, check, lib
+
+DEFAULT_MAX_GAP = 128
+DEFAULT_VOCAB_SPLIT = 16384
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FLH_BF16
+    if t.dtype == torch.float32:
+        return FLH_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on a HIP device")
+
+
+def _mask_u8(mask: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if mask is None:
+        return None
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    if mask.dtype != torch.uint8:
+        raise TypeError("loss_mask must be bool or uint8")
+    return mask.contiguous()
+
+
+def _f32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if t.dtype != torch.float32:
+        raise TypeError("upstream gradients, lse and entropy are float32")
+    return t.contiguous()
+
+
+def flh_abi_version() -> int:
+    return int(lib().flh_abi_version())
+
+
+def flh_tile_m(dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(lib().flh_tile_m(FLH_BF16 if dtype == torch.bfloat16 else FLH_F32))
+
+
+def flh_span_capacity(T: int, max_gap: int = DEFAULT_MAX_GAP) -> int:
+    return int(lib().flh_span_capacity(int(T), int(max_gap)))
+
+
+def flh_workspace_bytes(op: int, dtype: torch.dtype, T: int, H: int, V: int,
+                        vocab_split: int = 0) -> int:
+    code = FLH_BF16 if dtype == torch.bfloat16 else FLH_F32
+    return int(lib().flh_workspace_bytes(int(op), code, int(T), int(H), int(V), int(vocab_split)))
+
+
+@dataclass
+class ActiveMetaTensors:
+    """Device arrays of an flh_active_meta plus the host struct pointing at them."""
+    T: int
+    max_gap: int
+    tile_m: int
+    spans: torch.Tensor         # [span_cap, 2] int32
+    num_spans: torch.Tensor     # [1] int32
+    tile_bits: torch.Tensor     # [words] int32 holding uint32 bit patterns
+    active_count: torch.Tensor  # [1] int32
+    struct: ActiveMeta
+
+    def host_spans(self) -> List[Tuple[int, int]]:
+        n = int(self.num_spans.item())
+        return [tuple(x) for x in self.spans[:n].cpu().tolist()]
+
+    def host_bits(self) -> List[int]:
+        return [w & 0xFFFFFFFF for w in self.tile_bits.cpu().tolist()]
+
+
+def flh_spans_build(loss_mask: torch.Tensor, max_gap: int = DEFAULT_MAX_GAP,
+                    tile_m: Optional[int] = None, span_cap: Optional[int] = None) -> ActiveMetaTensors:
+    """Active metadata (tile bitmap, ordered spans, counts) built on the device."""
+    m = _mask_u8(loss_mask)
+    _require_cuda(m)
+    T = int(m.numel())
+    tm = flh_tile_m() if tile_m is None else int(tile_m)
+    cap = flh_span_capacity(T, max_gap) if span_cap is None else int(span_cap)
+    dev = m.device
+    n_tiles = (T + tm - 1) // tm if tm > 0 else 0
+    spans = torch.empty((max(cap, 1), 2), dtype=torch.int32, device=dev)
+    num = torch.empty(1, dtype=torch.int32, device=dev)
+    bits = torch.empty(max((n_tiles + 31) // 32, 1), dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    st = ActiveMeta(T, int(max_gap), tm, cap, spans.data_ptr(), num.data_ptr(), bits.data_ptr(),
+                    cnt.data_ptr())
+    check(lib().flh_spans_build(_ptr(m), ctypes.byref(st), None, 0, _stream(dev)), "flh_spans_build")
+    return ActiveMetaTensors(T, int(max_gap), tm, spans, num, bits, cnt, st)
+
+
+def _workspace(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def flh_forward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                workspace: Optional[torch.Tensor] = None):
+    """Returns (logprob, entropy, lse), each float32 [T]."""
+    _require_cuda(h, W, targets)
+    if h.dtype != W.dtype:
+        raise TypeError("h and W must share a dtype")
+    h, W = h.contiguous(), W.contiguous()
+    targets = targets.to(torch.int64).contiguous()
+    T, H = h.shape
+    V = W.shape[0]
+    if W.shape[1] != H or targets.numel() != T:
+        raise ValueError("shape mismatch")
+    dev = h.device
+    lp = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    need = flh_workspace_bytes(OP_FORWARD, h.dtype, T, H, V)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    check(lib().flh_forward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), T, H, V, _ptr(lp),
+                            _ptr(ent), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "flh_forward")
+    return lp, ent, lse
+
+
+def flh_backward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
+                 entropy: torch.Tensor, grad_logprob: Optional[torch.Tensor],
+                 grad_entropy: Optional[torch.Tensor], loss_mask: Optional[torch.Tensor] = None,
+                 meta: Optional[ActiveMetaTensors] = None, vocab_split: int = 0,
+                 workspace: Optional[torch.Tensor] = None):
+    """Returns (d_hidden [T,H], d_weight [V,H]) in the dtype of h."""
+    _require_cuda(h, W, targets, lse, entropy, grad_logprob, grad_entropy, loss_mask)
+    h, W = h.contiguous(), W.contiguous()
+    targets = targets.to(torch.int64).contiguous()
+    lse, entropy = _f32(lse), _f32(entropy)
+    g_lp, g_ent = _f32(grad_logprob), _f32(grad_entropy)
+    m = _mask_u8(loss_mask)
+    T, H = h.shape
+    V = W.shape[0]
+    dev = h.device
+    dH = torch.empty((T, H), dtype=h.dtype, device=dev)
+    dW = torch.empty((V, H), dtype=h.dtype, device=dev)
+    need = flh_workspace_bytes(OP_BACKWARD, h.dtype, T, H, V, vocab_split)
+    if need == 0:
+        raise ValueError("invalid sizes or vocab_split")
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    mp = ctypes.byref(meta.struct) if meta is not None else None
+    check(lib().flh_backward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), _ptr(lse),
+                             _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V,
+                             int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+                             _stream(dev)), "flh_backward")
+    return dH, dW
+
+
+# ---- tracing -------------------------------------------------------------------
+
+def trace_begin(capacity: int = 4096) -> None:
+    check(lib().flh_trace_begin(int(capacity)), "flh_trace_begin")
+
+
+def trace_end(max_records: int = 4096):
+    """Waits for the traced launches; returns [(kernel_name, split, ms), ...]."""
+    recs = (_lib.TraceRecord * max_records)()
+    n = lib().flh_trace_end(recs, max_records)
+    if n < 0:
+        raise _lib.FlhError(8, "flh_trace_end")
+    out = []
+    for i in range(min(n, max_records)):
+        r = recs[i]
+        out.append((lib().flh_kernel_name(r.kernel_id).decode(), int(r.split), float(r.ms)))
+    return out
+
+
+# ---- autograd ------------------------------------------------------------------
+
+class FusedLMHead(torch.autograd.Function):
+    """(logprob, entropy) = fused LM head(h, W, targets); backward through the
+    block-sparse path when a loss mask is given."""
+
+    @staticmethod
+    def forward(ctx, h, W, targets, loss_mask, max_gap, vocab_split):
+        lp, ent, lse = flh_forward(h, W, targets)
+        meta = flh_spans_build(loss_mask, max_gap) if loss_mask is not None else None
+        ctx.save_for_backward(h, W, targets, lse, ent, _mask_u8(loss_mask) if loss_mask is not None else None)
+        ctx.meta = meta
+        ctx.vocab_split = vocab_split
+        return lp, ent
+
+    @staticmethod
+    def backward(ctx, g_lp, g_ent):
+        h, W, targets, lse, ent, m = ctx.saved_tensors
+        g_lp = None if g_lp is None else g_lp.float().contiguous()
+        g_ent = None if g_ent is None else g_ent.float().contiguous()
+        dH, dW = flh_backward(h, W, targets, lse, ent, g_lp, g_ent, m, ctx.meta, ctx.vocab_split)
+        return dH, dW, None, None, None, None
+
+
+def fused_lm_head(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                  loss_mask: Optional[torch.Tensor] = None, max_gap: int = DEFAULT_MAX_GAP,
+                  vocab_split: int = 0):
+    """Per-token (logprob, entropy) of the LM head h W^T, differentiable in h and W."""
+    return FusedLMHead.apply(h, W, targets, loss_mask, max_gap, vocab_split)

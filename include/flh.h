@@ -1,0 +1,204 @@
+/*
+ * flh.h -- C ABI of the block-sparse fused LM head for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described on the page "perf(megatron): add
+ * block-sparse fused LM-head backward" (NovaSky-AI/SkyRL pull request 2376,
+ * cited below as "SkyRL #2376" with the page's section headings):
+ *
+ *   forward   z = h W^T computed tile by tile, never stored as [T, V]; an online
+ *             log-softmax gives each token's target log-prob and entropy
+ *             ("What does this PR do?", Bugbot "Overview": fused linear log-prob;
+ *             the stack's "fuse LM-head entropy for RL" layer).
+ *   metadata  a forward active mask (here a tile bitmap) and ordered active spans,
+ *             runs of the loss mask coalesced across gaps <= 128 tokens
+ *             ("How it works"; Bugbot "Overview").
+ *   backward  d-logits recomputed only for active token tiles; the hidden gradient
+ *             accumulated span by span, split by split (Gemini "Code Review":
+ *             d_hidden += split_d_logits @ split_weight); the final vocabulary
+ *             split staged at its live width with every launch sized from that
+ *             width (Greptile "Wide-tail grid exceeds live split"); the weight
+ *             gradient a dense contraction over all tokens ("How it works").
+ *
+ * Definitions (fp32 accumulation; inputs bf16 or fp32):
+ *   lse[t]     = log sum_v exp(z[t,v])
+ *   logprob[t] = z[t, targets[t]] - lse[t]
+ *   entropy[t] = sum_v p[t,v] (lse[t] - z[t,v]),  p = exp(z - lse)   (nats)
+ *   ga = m * grad_logprob, gb = m * grad_entropy  (m = loss mask, NULL grad = 0)
+ *   dz[t,v]    = ga[t] ([v == y_t] - p) + gb[t] p (lse[t] - entropy[t] - z[t,v])
+ *   d_hidden   = dz W,  d_weight = dz^T h
+ *
+ * Conventions (every entry point):
+ *   - All array arguments are DEVICE pointers into memory the caller owns; the
+ *     library never allocates or frees device memory and keeps no per-call
+ *     state.  Scratch memory is the caller's workspace (`ws`, `ws_bytes`), sized
+ *     by flh_workspace_bytes() and at least 256-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is only enqueued: no host/device synchronisation, no device-to-host reads,
+ *     so a whole forward+backward can be captured into a HIP graph.
+ *   - Matrices are row-major and contiguous: h [T,H], W [V,H], d_hidden [T,H],
+ *     d_weight [V,H].  h, W, d_hidden, d_weight must be 16-byte aligned and H a
+ *     multiple of 16 bytes of elements (8 for bf16, 4 for fp32).
+ *   - Every argument is checked on the host before anything is launched; a bad
+ *     argument returns an error status and enqueues nothing.  FLH_E_HIP means a
+ *     launch failed (its work may be partially enqueued).  Nothing aborts and no
+ *     exception crosses the ABI.
+ *   - Not checked (that would need a device read): targets in [0, V) (a target
+ *     out of range gives logprob = NaN for that token), finite inputs, and that
+ *     `meta` was built from the same loss mask.
+ *   - Results are bit-identical from run to run (no floating-point atomics).
+ *   - Calls on different streams may run concurrently if their buffers differ.
+ */
+#ifndef FLH_H_
+#define FLH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLH_ABI_VERSION 1
+
+typedef enum {
+  FLH_OK = 0,
+  FLH_E_NULL = 1,        /* a required pointer is NULL                               */
+  FLH_E_SHAPE = 2,       /* a size is <= 0, too large, or not a supported multiple   */
+  FLH_E_DTYPE = 3,       /* unknown dtype                                            */
+  FLH_E_ALIGN = 4,       /* a matrix pointer or the workspace is misaligned          */
+  FLH_E_WORKSPACE = 5,   /* ws_bytes smaller than flh_workspace_bytes()              */
+  FLH_E_META = 6,        /* active metadata inconsistent with this call              */
+  FLH_E_UNSUPPORTED = 7, /* valid request this build does not support                */
+  FLH_E_HIP = 8          /* a HIP runtime call or kernel launch failed               */
+} flh_status;
+
+typedef enum { FLH_F32 = 0, FLH_BF16 = 1 } flh_dtype;
+
+/* Which call a workspace size is for. */
+typedef enum { FLH_OP_SPANS = 0, FLH_OP_FORWARD = 1, FLH_OP_BACKWARD = 2 } flh_op;
+
+/*
+ * Active metadata derived from the loss mask (SkyRL #2376, "How it works": one
+ * builder derives the forward active mask and the backward spans).  The struct
+ * itself is host memory; every pointer in it is device memory owned by the
+ * caller.  The caller fills T, max_gap, tile_m, span_cap and the four pointers;
+ * flh_spans_build fills the arrays.
+ *
+ *   spans       [span_cap][2] int32, half-open (start, end) in flat packed token
+ *               coordinates, ascending and disjoint.  A span starts and ends on an
+ *               active token; two consecutive runs of active tokens share a span
+ *               iff at most max_gap inactive tokens lie between them (Bugbot
+ *               "Overview": gaps <= 128).  Sequence boundaries are not seen.
+ *   num_spans   device int32 scalar: number of spans written.
+ *   tile_bits   [ceil(ceil(T/tile_m)/32)] uint32; bit i%32 of word i/32 (least
+ *               significant first) is set iff any token of
+ *               [i*tile_m, min(T,(i+1)*tile_m)) is active.  Unused bits are 0.
+ *   active_count device int32 scalar: number of active tokens A.
+ */
+typedef struct {
+  int64_t T;            /* tokens the metadata describes                             */
+  int32_t max_gap;      /* G >= 0 (the page uses 128)                                */
+  int32_t tile_m;       /* bitmap tile height; flh_backward requires flh_tile_m(dt)  */
+  int64_t span_cap;     /* capacity of `spans`, >= flh_span_capacity(T, max_gap)     */
+  int32_t *spans;
+  int32_t *num_spans;
+  uint32_t *tile_bits;
+  int32_t *active_count;
+} flh_active_meta;
+
+/* ABI version of the loaded library (FLH_ABI_VERSION it was built with). */
+int32_t flh_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *flh_status_string(flh_status s);
+
+/* Token-tile height of the d-logits tile skip: the tile_m flh_backward expects. */
+int32_t flh_tile_m(flh_dtype dt);
+
+/* Largest possible number of spans: floor((T + G + 1) / (G + 2)); 0 for T <= 0. */
+int64_t flh_span_capacity(int64_t T, int32_t max_gap);
+
+/*
+ * Workspace bytes the call `op` needs for these sizes (0 for FLH_OP_SPANS).
+ * vocab_split 0 means 16384.  Returns 0 for invalid sizes as well.
+ */
+size_t flh_workspace_bytes(flh_op op, flh_dtype dt, int64_t T, int64_t H, int64_t V,
+                           int32_t vocab_split);
+
+/*
+ * Builds the active metadata from the loss mask on the device.
+ *   loss_mask  [T] uint8, nonzero = active (the RL loss mask, Bugbot "Overview").
+ *   meta       host struct, see flh_active_meta; meta->T is the length of the mask.
+ * Errors: FLH_E_NULL (mask, meta or a meta pointer NULL), FLH_E_SHAPE (T <= 0 or
+ * T >= 2^31, tile_m <= 0), FLH_E_META (max_gap < 0 or span_cap too small).
+ */
+flh_status flh_spans_build(const uint8_t *loss_mask, flh_active_meta *meta, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/*
+ * Forward: per-token target log-prob, entropy and log-sum-exp, never storing the
+ * [T, V] logits (SkyRL #2376, "What does this PR do?"; fused entropy layer).
+ *   dt        FLH_BF16 or FLH_F32, the dtype of h and W.
+ *   h [T,H], W [V,H], targets [T] int64 in [0, V).
+ *   logprob, entropy, lse: [T] fp32 outputs (lse and entropy are what
+ *   flh_backward needs saved).
+ *   ws        at least flh_workspace_bytes(FLH_OP_FORWARD, dt, T, H, V, 0) bytes.
+ */
+flh_status flh_forward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                       int64_t T, int64_t H, int64_t V, float *logprob, float *entropy,
+                       float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward: d_hidden [T,H] and d_weight [V,H] (dtype dt, both overwritten) from
+ * the upstream gradients of logprob and entropy.
+ *   lse, entropy   [T] fp32 as written by flh_forward for the same inputs.
+ *   grad_logprob   [T] fp32 or NULL (zero).
+ *   grad_entropy   [T] fp32 or NULL (zero: the no-grad entropy mode).
+ *   loss_mask      [T] uint8 or NULL (all tokens active).  Gradients of inactive
+ *                  tokens are ignored and their d_hidden rows are exactly +0.
+ *   meta           NULL: dense fallback (every token tile computed, dense hidden
+ *                  projection; SkyRL #2376 "Overview": the full dense projection
+ *                  when no spans are provided).  Otherwise metadata built from
+ *                  `loss_mask` by flh_spans_build: d-logits tiles without an active
+ *                  token are skipped and d_hidden is projected over the spans only
+ *                  ("How it works").  Requires loss_mask != NULL, meta->T == T and
+ *                  meta->tile_m == flh_tile_m(dt), else FLH_E_META.
+ *   vocab_split    split width S (0 = 16384), a multiple of 256.  Split s covers
+ *                  vocabulary rows [s*S, s*S + W_s) with W_s = min(S, V - s*S); its
+ *                  d-logits staging buffer and every launch over it are sized by
+ *                  the live width W_s (SkyRL #2376, "How it works" and the Greptile
+ *                  finding on the wide-tail grid).
+ *   ws             at least flh_workspace_bytes(FLH_OP_BACKWARD, dt, T, H, V,
+ *                  vocab_split) bytes.
+ */
+flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                        const float *lse, const float *entropy, const float *grad_logprob,
+                        const float *grad_entropy, const uint8_t *loss_mask,
+                        const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
+                        int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * Launch tracing (profiling aid).  Between flh_trace_begin and flh_trace_end on
+ * the same host thread, every kernel launch of the calls above is bracketed by a
+ * pair of HIP events recorded on that call's stream (at most `capacity`
+ * launches; later ones are not traced).  flh_trace_end waits for the events,
+ * writes up to max_records records and returns how many launches were traced
+ * (or -1 on a HIP error).  Tracing creates HIP events, so it is not for use
+ * under graph capture.
+ */
+typedef struct {
+  int32_t kernel_id;    /* see flh_kernel_name                                      */
+  int32_t split;        /* vocabulary split index, -1 when not split-local          */
+  float ms;             /* elapsed time between the two events                      */
+} flh_trace_record;
+
+flh_status flh_trace_begin(int32_t capacity);
+int32_t flh_trace_end(flh_trace_record *records, int32_t max_records);
+const char *flh_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLH_H_ */

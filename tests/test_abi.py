@@ -1,0 +1,151 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/flh.h declares, and rejects bad arguments on the host before any
+launch (no GPU is touched: every call here fails validation first)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from entropy_block_sparse_amd import _lib
+from entropy_block_sparse_amd._lib import ActiveMeta, lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "flh.h")
+
+E = {v: k for k, v in _lib.STATUS_NAMES.items()}
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10008)  # not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"\b(flh_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "flh_spans_build" in names and "flh_forward" in names and "flh_backward" in names
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert {n for n, _, _ in _lib.SIGNATURES} == set(names)
+
+
+def test_abi_version_and_queries():
+    L = lib()
+    assert L.flh_abi_version() == 1
+    assert L.flh_tile_m(1) == 128 and L.flh_tile_m(0) == 128 and L.flh_tile_m(7) == 0
+    assert L.flh_span_capacity(16384, 128) == 127
+    assert L.flh_span_capacity(262144, 128) == 2017
+    assert L.flh_span_capacity(0, 128) == 0 and L.flh_span_capacity(10, -1) == 0
+    for s in range(9):
+        assert L.flh_status_string(s)
+
+
+def test_span_capacity_matches_oracle():
+    from oracle import spans as S
+    L = lib()
+    for T in (1, 2, 7, 100, 512, 16384, 65536):
+        for G in (0, 1, 5, 47, 128):
+            assert L.flh_span_capacity(T, G) == S.span_capacity(T, G)
+
+
+def test_workspace_sizes():
+    L = lib()
+    f = L.flh_workspace_bytes
+    # forward: one 16-byte softmax state per (256-row vocabulary tile, token)
+    assert f(1, 1, 16384, 4096, 128256, 0) == ((128256 + 255) // 256) * 16384 * 16
+    b = f(2, 1, 16384, 4096, 128256, 0)
+    assert b >= 16384 * 16384 * 2 + 16384 * 4096 * 4   # staging + fp32 accumulator
+    assert f(2, 1, 512, 256, 4096, 0) < f(2, 1, 512, 256, 40960, 0)
+    # the staging buffer follows the live width: a vocabulary narrower than the split
+    assert f(2, 1, 1000, 64, 1000, 16384) < f(2, 1, 1000, 64, 20000, 16384)
+    assert f(0, 1, 100, 64, 100, 0) == 0                 # spans need none
+    for bad in [(1, 1, 0, 64, 100, 0), (1, 1, 100, 60, 100, 0), (2, 1, 100, 64, 100, 100),
+                (1, 9, 100, 64, 100, 0), (1, 1, 100, 64, 0, 0), (1, 0, 100, 66, 100, 0)]:
+        assert f(*bad) == 0, bad
+
+
+def _meta(T=100, G=128, tm=128, cap=None, spans=FAKE, num=FAKE, bits=FAKE, cnt=FAKE):
+    return ActiveMeta(T, G, tm, (T + G + 1) // (G + 2) if cap is None else cap,
+                      spans.value if spans else None, num.value if num else None,
+                      bits.value if bits else None, cnt.value if cnt else None)
+
+
+def test_spans_build_validation():
+    L = lib()
+    call = lambda mask, m: L.flh_spans_build(mask, ctypes.byref(m) if m is not None else None, None, 0, None)
+    assert call(None, _meta()) == E["FLH_E_NULL"]
+    assert call(FAKE, None) == E["FLH_E_NULL"]
+    assert call(FAKE, _meta(spans=None)) == E["FLH_E_NULL"]
+    assert call(FAKE, _meta(cnt=None)) == E["FLH_E_NULL"]
+    assert call(FAKE, _meta(T=0, cap=0)) == E["FLH_E_SHAPE"]
+    assert call(FAKE, _meta(T=1 << 31, cap=10 ** 9)) == E["FLH_E_SHAPE"]
+    assert call(FAKE, _meta(tm=0)) == E["FLH_E_SHAPE"]
+    assert call(FAKE, _meta(G=-1, cap=100)) == E["FLH_E_META"]
+    assert call(FAKE, _meta(T=1000, G=0, cap=499)) == E["FLH_E_META"]   # needs 500
+
+
+def _fwd(dt=1, h=FAKE, W=FAKE, y=FAKE, T=512, H=256, V=4096, lp=FAKE, ent=FAKE, lse=FAKE,
+         ws=FAKE, nbytes=1 << 40):
+    return lib().flh_forward(dt, h, W, y, T, H, V, lp, ent, lse, ws, nbytes, None)
+
+
+def test_forward_validation():
+    assert _fwd(dt=5) == E["FLH_E_DTYPE"]
+    for k in ("h", "W", "y", "lp", "ent", "lse", "ws"):
+        assert _fwd(**{k: None}) == E["FLH_E_NULL"], k
+    assert _fwd(T=0) == E["FLH_E_SHAPE"]
+    assert _fwd(V=0) == E["FLH_E_SHAPE"]
+    assert _fwd(T=1 << 31) == E["FLH_E_SHAPE"]
+    assert _fwd(H=12) == E["FLH_E_SHAPE"]            # bf16 rows must be 16-byte multiples
+    assert _fwd(dt=0, H=6) == E["FLH_E_SHAPE"]
+    assert _fwd(h=FAKE_ODD) == E["FLH_E_ALIGN"]
+    assert _fwd(W=FAKE_ODD) == E["FLH_E_ALIGN"]
+    assert _fwd(ws=ctypes.c_void_p(0x10010)) == E["FLH_E_ALIGN"]
+    assert _fwd(nbytes=100) == E["FLH_E_WORKSPACE"]
+
+
+def _bwd(dt=1, h=FAKE, W=FAKE, y=FAKE, lse=FAKE, ent=FAKE, glp=FAKE, gent=FAKE, mask=FAKE,
+         meta="ok", T=512, H=256, V=4096, split=0, dH=FAKE, dW=FAKE, ws=FAKE, nbytes=1 << 40):
+    m = _meta(T=512) if meta == "ok" else meta
+    mp = ctypes.byref(m) if m is not None else None
+    return lib().flh_backward(dt, h, W, y, lse, ent, glp, gent, mask, mp, T, H, V, split,
+                              dH, dW, ws, nbytes, None)
+
+
+def test_backward_validation():
+    assert _bwd(dt=3) == E["FLH_E_DTYPE"]
+    for k in ("h", "W", "y", "lse", "ent", "dH", "dW", "ws"):
+        assert _bwd(**{k: None}) == E["FLH_E_NULL"], k
+    assert _bwd(split=100) == E["FLH_E_SHAPE"]            # not a multiple of 256
+    assert _bwd(split=-256) == E["FLH_E_SHAPE"]
+    assert _bwd(H=0) == E["FLH_E_SHAPE"]
+    # metadata must match the call (the page: spans are rejected when the layout
+    # changes their coordinates)
+    assert _bwd(mask=None) == E["FLH_E_META"]
+    assert _bwd(meta=_meta(T=511)) == E["FLH_E_META"]
+    assert _bwd(meta=_meta(T=512, tm=64)) == E["FLH_E_META"]
+    assert _bwd(meta=_meta(T=512, spans=None)) == E["FLH_E_NULL"]
+    assert _bwd(dH=FAKE_ODD) == E["FLH_E_ALIGN"]
+    assert _bwd(dW=FAKE_ODD) == E["FLH_E_ALIGN"]
+    assert _bwd(nbytes=1000) == E["FLH_E_WORKSPACE"]
+
+
+def test_python_binding_names_match_abi():
+    import entropy_block_sparse_amd as pkg
+    for n in ("flh_spans_build", "flh_forward", "flh_backward", "flh_workspace_bytes",
+              "flh_span_capacity", "flh_tile_m", "flh_abi_version"):
+        assert callable(getattr(pkg, n))
+
+
+def test_product_path_does_not_import_oracle():
+    pkg_dir = os.path.join(os.path.dirname(HEADER), "..", "entropy_block_sparse_amd")
+    for root, _, files in os.walk(pkg_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(root, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
