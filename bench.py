@@ -1,0 +1,209 @@
+"""Benchmark: fused LM-head forward + backward throughput on one MI355X.
+
+One step = flh_spans_build + flh_forward + flh_backward over one synthetic packed
+batch (inputs resident in HBM).  Prints one JSON line:
+
+  value      tokens/s of the whole step (T * steps / elapsed)
+  roofline   the dominant kernel's algorithmic flops per launch / its mean launch
+             time (HIP events around each launch on the launch stream), against
+             the bf16 dense MFMA peak; `traffic` is the measured HBM bytes per
+             launch from the committed rocprofv3 counter summary when it was taken
+             on the current kernel source, else null
+  cpu_baseline  the fp64 oracle timed on the host cores on a token slice of the
+             same workload
+
+Default workload: the Llama-3-8B-like head (T=16384, H=4096, V=128256, bf16,
+about 45% of tokens active).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2516.6e12     # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP32_MATRIX = 157.3e12
+HBM_PEAK = 8.0e12
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--active-frac", type=float, default=None, help="stress workload point")
+    p.add_argument("--dense", action="store_true", help="dense fallback (no metadata)")
+    p.add_argument("--cpu-tokens", type=int, default=256, help="oracle slice (0 = skip)")
+    p.add_argument("--no-trace", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "entropy_block_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    rec = d.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(h, W, y, mask, a, b, n_tok):
+    """The fp64 oracle (forward + backward) on the first n_tok tokens, full H and V."""
+    import threadpoolctl
+
+    from oracle import lmhead as O
+
+    hs = h[:n_tok].float().cpu().numpy().astype(np.float64)
+    Wf = W.float().cpu().numpy().astype(np.float64)
+    ys = y[:n_tok].cpu().numpy()
+    ms = mask[:n_tok]
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    O.forward(hs, Wf, ys)
+    O.backward(hs, Wf, ys, ms, a[:n_tok], None if b is None else b[:n_tok])
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the workload at full H and V, fp64 numpy "
+                      f"forward+backward, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    from entropy_block_sparse_amd import (flh_backward, flh_forward, flh_spans_build,
+                                          flh_workspace_bytes, trace_begin, trace_end)
+    from oracle import spans as S
+    from workloads import get_config, make_mask, make_tensors, make_upstream
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    mask_np, minfo = make_mask(cfg.cid, active_frac=args.active_frac)
+    T, H, V, Ssplit = cfg.T, cfg.H, cfg.V, cfg.vocab_split
+    h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
+    a_np, b_np = make_upstream(mask_np)
+    mask = torch.as_tensor(mask_np).to(dev)
+    g_lp = torch.as_tensor(a_np).to(dev)
+    g_ent = torch.as_tensor(b_np).to(dev)
+    ws_f = torch.empty(flh_workspace_bytes(1, h.dtype, T, H, V), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(flh_workspace_bytes(2, h.dtype, T, H, V, Ssplit), dtype=torch.uint8, device=dev)
+
+    def step():
+        meta = None if args.dense else flh_spans_build(mask)
+        lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
+        dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b)
+        return dH, dW
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    trace = not args.no_trace
+    if trace:
+        trace_begin(64 * args.steps + 64)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    recs = trace_end(64 * args.steps + 64) if trace else []
+
+    # ---- algorithmic work of the method ----
+    flags = S.tile_flags(mask_np, 128)
+    T_at = sum(flags) * 128 - (128 * len(flags) - T if flags and flags[-1] else 0)
+    spans = S.active_spans(mask_np, 128)
+    T_sp = sum(e - s for s, e in spans)
+    A = int(mask_np.sum())
+    pass_flops = 2.0 * H * V
+    F_method = pass_flops * (T + T_at + T_sp + T) if not args.dense else pass_flops * 4 * T
+    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32_MATRIX
+
+    per_kernel = {}
+    for name, split, kms in recs:
+        d = per_kernel.setdefault(name, {"launches": 0, "ms": 0.0})
+        d["launches"] += 1
+        d["ms"] += kms
+    for d in per_kernel.values():
+        d["ms_per_step"] = d["ms"] / args.steps
+        d["ms_per_launch"] = d["ms"] / max(1, d["launches"])
+    # algorithmic flops per launch of each contraction kernel
+    n_splits = -(-V // Ssplit)
+    alg = {
+        "fwd_logits_softmax": pass_flops * T,
+        "dweight": pass_flops * T / n_splits,
+        "dlogits": pass_flops * T_at / n_splits,
+        "dhidden_spans": pass_flops * T_sp / n_splits,
+    }
+    roof = None
+    if per_kernel:
+        dom = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k]["ms"])
+        achieved = alg[dom] / (per_kernel[dom]["ms_per_launch"] * 1e-3)
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": stored_traffic(dom, cfg.name)}
+        for k in per_kernel:
+            if k in alg:
+                per_kernel[k]["tflops"] = alg[k] / (per_kernel[k]["ms_per_launch"] * 1e-3) / 1e12
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(h, W, y, mask_np, a_np, b_np, min(args.cpu_tokens, T))
+
+    out = {
+        "metric": "fused LM-head fwd+bwd tokens/sec at 1 GPU + % of bf16 MFMA peak",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
+                   "active_frac": minfo["active_frac"], "mask_seed": minfo["seed"],
+                   "dense_fallback": bool(args.dense)},
+        "pct_peak_method": F_method / (ms * 1e-3) / peak,
+        "work": {"A": A, "T_at128": int(T_at), "T_sp": int(T_sp), "spans": len(spans),
+                 "F_method_tflop": F_method / 1e12, "F_dense_tflop": 4 * pass_flops * T / 1e12},
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
