@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--dense", action="store_true", help="dense fallback (no metadata)")
     p.add_argument("--cpu-tokens", type=int, default=256, help="oracle slice (0 = skip)")
     p.add_argument("--no-trace", action="store_true")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="run one device copy of this many MiB first (counter calibration)")
     return p.parse_args()
 
 
@@ -119,6 +121,15 @@ def main():
         lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
         dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b)
         return dH, dW
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

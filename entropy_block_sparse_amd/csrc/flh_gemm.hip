@@ -148,7 +148,8 @@ __device__ __forceinline__ void group_map(int64_t L, int64_t m_tiles, int64_t n_
 }
 
 template <typename T, int KIND>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
+    const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   constexpr int kPer = Elt<T>::kPer;       // elements per 16-byte chunk
   constexpr int kBK = 128 / sizeof(T);     // K elements per stage
@@ -416,51 +417,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
     load_stage(0);
     store_stage(0, 0);
     __syncthreads();
+    // Fragment reads are double-buffered: the 8 LDS reads of K slice q+1 are
+    // issued while the 16 MFMAs of slice q run, interleaved one read per two
+    // MFMAs, so LDS latency hides behind matrix-core work.
     const int frag_row = lane & 31;
+    const int a_frag = (wm * 128 + frag_row) * kRowBytes + g * 16;
+    const int b_frag = (wn * 128 + frag_row) * kRowBytes + g * 16;
+    // reads in the order the MFMAs consume them: A0, B0..B3, A1..A3
+    auto read_frags = [&](const char *As, const char *Bs, int q, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+      fa[0] = *reinterpret_cast<const u32x4 *>(As + a_frag + q * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const u32x4 *>(Bs + b_frag + j * 32 * kRowBytes + q * 32);
+#pragma unroll
+      for (int i = 1; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const u32x4 *>(As + a_frag + i * 32 * kRowBytes + q * 32);
+    };
     for (int kt = 0; kt < nk; ++kt) {
       const int st = kt & 1;
       if (kt + 1 < nk) load_stage(kt + 1);
       const char *As = smem + st * 2 * kOpBytes;
       const char *Bs = As + kOpBytes;
+      u32x4 fa[2][4], fb[2][4];
+      read_frags(As, Bs, 0, fa[0], fb[0]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int coff = (2 * q + g) * 16;
-        u32x4 fa[4], fb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[i] = *reinterpret_cast<const u32x4 *>(As + (wm * 128 + i * 32 + frag_row) * kRowBytes + coff);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          fb[j] = *reinterpret_cast<const u32x4 *>(Bs + (wn * 128 + j * 32 + frag_row) * kRowBytes + coff);
+        if (q < 3) read_frags(As, Bs, q + 1, fa[(q + 1) & 1], fb[(q + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
+          for (int j = 0; j < 4; ++j) Mma<T>::run(acc[i][j], fa[q & 1][i], fb[q & 1][j]);
+        if (q < 3) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (kt + 1 < nk) store_stage(st ^ 1, kt + 1);
       __syncthreads();
     }
 
     // ---------------- epilogues ----------------
-    // acc[i][j][r] holds output row   wm*128 + i*32 + 8*(r/4) + 4*g + (r%4)
-    //                  and column     wn*128 + j*32 + (lane % 32).
+    // acc[i][j][r] holds tile row  wm*128 + i*32 + 8*(r/4) + 4*g + (r%4)
+    //               and tile col  wn*128 + j*32 + (lane % 32).
+    // Indices below are tile-local 32-bit; tile origins are uniform.
+    const int row0 = wm * 128 + (g << 2);   // + i*32 + 8*(r/4) + (r%4)
+    const int col0 = wn * 128 + (lane & 31);  // + j*32
     if constexpr (KIND == kFwd) {
-      const int64_t vw = mi * kTile + wm * 128;  // first vocabulary row of this wave
-      const bool full = (mi * kTile + kTile) <= a.V;
+      const int64_t v_tile = mi * kTile;
+      const int n_rows = (a.V - v_tile) < kTile ? (int)(a.V - v_tile) : kTile;  // valid vocab rows
+      const bool full = n_rows == kTile;
+      const int64_t t_tile = ni * kTile;
       float4 *xch = reinterpret_cast<float4 *>(smem);
       float st_M[4], st_s[4], st_u[4], st_zy[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int col = wn * 128 + j * 32 + (lane & 31);
-        const int64_t t = ni * kTile + col;
-        const int64_t y = (t < a.T) ? a.targets[t] : -1;
+        const int col = col0 + j * 32;
+        const int64_t t = t_tile + col;
+        // target row local to this tile, or -1
+        int yl = -1;
+        if (t < a.T) {
+          const int64_t yd = a.targets[t] - v_tile;
+          yl = (yd >= 0 && yd < kTile) ? (int)yd : -1;
+        }
         float mx = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t v = vw + i * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
-            if (full || v < a.V) mx = fmaxf(mx, acc[i][j][r]);
+            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
+            if (full || row < n_rows) mx = fmaxf(mx, acc[i][j][r]);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         float s = 0.f, u = 0.f, zy = kNegInf;
@@ -468,15 +498,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t v = vw + i * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
+            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
             const float z = acc[i][j][r];
-            if (full || v < a.V) {
+            if (full || row < n_rows) {
               const float d = z - mx;
               const float e = __expf(d);
               s += e;
               u += e * d;
             }
-            if (v == y) zy = z;
+            if (row == yl) zy = z;
           }
         s += __shfl_xor(s, 32);
         u += __shfl_xor(u, 32);
@@ -489,29 +519,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
       }
       __syncthreads();
       if (wm == 0 && lane < 32) {
+        float4 *out = reinterpret_cast<float4 *>(a.part) + mi * a.T + t_tile;
+        const int n_cols = (a.T - t_tile) < kTile ? (int)(a.T - t_tile) : kTile;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = wn * 128 + j * 32 + lane;
-          const int64_t t = ni * kTile + col;
+          const int col = col0 + j * 32;
           const float4 o = xch[col];
           float M = st_M[j], s = st_s[j], u = st_u[j];
           merge_state(M, s, u, o.x, o.y, o.z);
           const float zy = fmaxf(st_zy[j], o.w);
-          if (t < a.T) reinterpret_cast<float4 *>(a.part)[mi * a.T + t] = make_float4(M, s, u, zy);
+          if (col < n_cols) out[col] = make_float4(M, s, u, zy);
         }
       }
     } else if constexpr (KIND == kDlogits) {
-      T *D = reinterpret_cast<T *>(a.D);
+      const int64_t v_tile = mi * kTile;                 // split-local first column
+      const int n_live = (a.Ws - v_tile) < kTile ? (int)(a.Ws - v_tile) : kTile;
+      const int n_cols = (a.ld_d - v_tile) < kTile ? (int)(a.ld_d - v_tile) : kTile;
+      T *Dt = reinterpret_cast<T *>(a.D) + v_tile;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int col = wn * 128 + j * 32 + (lane & 31);
+        const int col = col0 + j * 32;
         const int64_t e = 2 * ni + (col >> 7);
         const int64_t tile = (e < a.n_skip_tiles) ? a.tile_list[e] : -1;
         const int64_t t = tile * kSkipTile + (col & 127);
         const bool tok = tile >= 0 && t < a.T;
         bool act = false;
         float lse_t = 0.f, ez = 0.f, ga = 0.f, gb = 0.f;
-        int64_t y = -1;
+        int yl = -1;
         if (tok) {
           act = a.mask ? (a.mask[t] != 0) : true;
           if (act) {
@@ -519,54 +553,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs a) {
             ez = lse_t - a.entropy[t];
             ga = a.grad_lp ? a.grad_lp[t] : 0.f;
             gb = a.grad_ent ? a.grad_ent[t] : 0.f;
-            y = a.targets[t] - a.v_base;
+            const int64_t yd = a.targets[t] - a.v_base - v_tile;
+            yl = (yd >= 0 && yd < kTile) ? (int)yd : -1;
           }
         }
+        const int lim = act ? n_live : 0;   // columns >= lim are stored as 0
+        T *drow = Dt + t * a.ld_d;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int64_t v0 = mi * kTile + wm * 128 + i * 32 + q * 8 + g * 4;
+            const int c0 = row0 + i * 32 + q * 8;  // first of 4 consecutive columns
             float d[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const float z = acc[i][j][4 * q + c];
-              const int64_t v = v0 + c;
               const float p = __expf(z - lse_t);
-              const float val = ga * ((v == y ? 1.f : 0.f) - p) + gb * p * (ez - z);
-              d[c] = (act && v < a.Ws) ? val : 0.f;
+              const float val = ga * ((c0 + c == yl ? 1.f : 0.f) - p) + gb * p * (ez - z);
+              d[c] = (c0 + c < lim) ? val : 0.f;
             }
-            if (tok && v0 < a.ld_d) store4(D + t * a.ld_d + v0, d[0], d[1], d[2], d[3]);
+            if (tok && c0 < n_cols) store4(drow + c0, d[0], d[1], d[2], d[3]);
           }
       }
     } else if constexpr (KIND == kDhidden) {
+      const int n_rows = (int)(span_s1 - span_s0);
+      const int64_t n_tile = ni * kTile;
+      const int n_cols = (a.H - n_tile) < kTile ? (int)(a.H - n_tile) : kTile;
+      float *base = a.dh_acc + span_s0 * a.H + n_tile;
+      const uint32_t ldh = (uint32_t)a.H;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t t = span_s0 + wm * 128 + i * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
-          if (t >= span_s1) continue;
+          const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
+          if (row >= n_rows) continue;
+          float *prow = base + (uint32_t)row * ldh;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int64_t n = ni * kTile + wn * 128 + j * 32 + (lane & 31);
-            if (n < a.H) {
-              float *p = a.dh_acc + t * a.H + n;
-              *p = a.first_split ? acc[i][j][r] : *p + acc[i][j][r];
-            }
+            const int col = col0 + j * 32;
+            if (col < n_cols) prow[col] = a.first_split ? acc[i][j][r] : prow[col] + acc[i][j][r];
           }
         }
     } else {
-      T *dW = reinterpret_cast<T *>(a.dW);
+      const int64_t v_tile = mi * kTile;
+      const int n_rows = (a.Ws - v_tile) < kTile ? (int)(a.Ws - v_tile) : kTile;
+      const int64_t n_tile = ni * kTile;
+      const int n_cols = (a.H - n_tile) < kTile ? (int)(a.H - n_tile) : kTile;
+      T *base = reinterpret_cast<T *>(a.dW) + (a.v_base + v_tile) * a.H + n_tile;
+      const uint32_t ldw = (uint32_t)a.H;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t v = mi * kTile + wm * 128 + i * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
-          if (v >= a.Ws) continue;
+          const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
+          if (row >= n_rows) continue;
+          T *prow = base + (uint32_t)row * ldw;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int64_t n = ni * kTile + wn * 128 + j * 32 + (lane & 31);
-            if (n < a.H) store1(dW + (a.v_base + v) * a.H + n, acc[i][j][r]);
+            const int col = col0 + j * 32;
+            if (col < n_cols) store1(prow + col, acc[i][j][r]);
           }
         }
     }
