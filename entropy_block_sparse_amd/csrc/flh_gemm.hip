@@ -47,6 +47,11 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = 144;               // LDS tile row: 128 B of K + 16 B pad
 constexpr int kOpBytes = kTile * kRowBytes;  // one operand tile, one stage
 constexpr int kLdsBytes = 4 * kOpBytes;      // A and B, two stages (147456 B)
+// bf16 path: a ring of kNS stages of 32 K elements (64 B per row) per operand.
+constexpr int kNS = 4;
+constexpr int kOpStage = kTile * 64;         // one operand, one stage: 16 KiB
+constexpr int kStage = 2 * kOpStage;         // 32 KiB
+constexpr int kLdsBytesV2 = kNS * kStage;    // 128 KiB
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <typename T> struct Elt;
@@ -135,14 +140,14 @@ __device__ __forceinline__ void merge_state(float &M, float &s, float &u, float 
 }
 
 // Position of linear tile id L in an (m_tiles x n_tiles) grid walked in groups of
-// 8 m-tiles, m fastest: 32 consecutive ids form an 8 x 4 block.
-__device__ __forceinline__ void group_map(int64_t L, int64_t m_tiles, int64_t n_tiles,
+// GM m-tiles, m fastest: 32 consecutive ids form a GM x 32/GM block.
+__device__ __forceinline__ void group_map(int64_t L, int64_t m_tiles, int64_t n_tiles, int64_t GM,
                                           int64_t &mi, int64_t &ni) {
-  const int64_t per_group = 8 * n_tiles;
+  const int64_t per_group = GM * n_tiles;
   const int64_t g = L / per_group;
   const int64_t r = L - g * per_group;
-  const int64_t first = g * 8;
-  const int64_t gm = (m_tiles - first) < 8 ? (m_tiles - first) : 8;
+  const int64_t first = g * GM;
+  const int64_t gm = (m_tiles - first) < GM ? (m_tiles - first) : GM;
   mi = first + r % gm;
   ni = r / gm;
 }
@@ -150,7 +155,8 @@ __device__ __forceinline__ void group_map(int64_t L, int64_t m_tiles, int64_t n_
 template <typename T, int KIND>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
     const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  constexpr bool kV2 = sizeof(T) == 2;  // bf16: LDS-direct ring; fp32: register-staged
+  __shared__ __attribute__((aligned(16))) char smem[kV2 ? kLdsBytesV2 : kLdsBytes];
   constexpr int kPer = Elt<T>::kPer;       // elements per 16-byte chunk
   constexpr int kBK = 128 / sizeof(T);     // K elements per stage
   constexpr bool kATr = (KIND == kDweight);
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1;
   const int wn = wave & 1;
   const int g = lane >> 5;
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       L = r * G + (b & 7) * (G >> 3) + (b >> 3);
     }
     int64_t mi, ni;
-    group_map(L, m_tiles, n_tiles, mi, ni);
+    group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : 8, mi, ni);
 
     int64_t span_s0 = 0, span_s1 = 0;
     if constexpr (KIND == kDhidden) {
@@ -238,6 +244,37 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       span_s1 = a.span_tiles[2 * mi + 1];
     }
 
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    if constexpr (KIND == kDhidden) {
+      // Splits after the first continue the fp32 sum of the earlier splits: start the
+      // accumulators from it, so the epilogue is a plain store.
+      if (!a.first_split) {
+        const int n_rows = (int)(span_s1 - span_s0);
+        const int64_t n_tile = ni * kTile;
+        const int n_cols = (a.H - n_tile) < kTile ? (int)(a.H - n_tile) : kTile;
+        const float *base = a.dh_acc + span_s0 * a.H + n_tile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * 128 + (g << 2) + i * 32 + ((r >> 2) << 3) + (r & 3);
+            const float *prow = base + (uint32_t)(row < n_rows ? row : 0) * (uint32_t)a.H;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int col = wn * 128 + (lane & 31) + j * 32;
+              acc[i][j][r] = (row < n_rows && col < n_cols) ? prow[col] : 0.f;
+            }
+          }
+      }
+    }
+
+    if constexpr (!kV2) {
     // ---------------- operand addressing ----------------
     // Uniform 64-bit bases (tile origin at K = 0) plus 32-bit per-thread byte
     // offsets.  Rows past the end of an operand are clamped onto its last row:
@@ -406,14 +443,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       else store_rows(Bs, rb, kt);
     };
 
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
     load_stage(0);
     store_stage(0, 0);
     __syncthreads();
@@ -459,6 +488,265 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       }
       if (kt + 1 < nk) store_stage(st ^ 1, kt + 1);
       __syncthreads();
+    }
+
+    } else {
+      // ================= bf16: LDS-direct loads into a kNS-stage ring =================
+      // Each stage holds 32 K elements of both operands.  Loads go straight from
+      // global memory into LDS (buffer_load ... lds: lane l of a wave writes 16 bytes
+      // at the instruction's LDS base + 16 l), kNS-1 stages ahead of the MFMAs, so no
+      // VGPRs stage the data and no LDS stores are issued.  Buffer descriptors bound
+      // every operand: rows past its end read as zero.
+      //
+      // Row-form operands (K contiguous in memory: W, h, the d-logits rows) are stored
+      // as [256 rows][4 chunks of 16 B]; logical chunk c of row r sits at position
+      // c ^ swz_row(r), which spreads the 16 rows read together by an MFMA fragment
+      // read over distinct banks.  Transposed operands (K = the row index in memory:
+      // W for dHidden, the d-logits and h for dWeight) are stored as loaded, as
+      // [32 K rows][32 chunks of 16 B along M], chunk c of K row k at c ^ (4 (k % 4)),
+      // and turned into K-contiguous fragments by ds_read_b64_tr_b16: within a group
+      // of 16 lanes, lane i reads 4 consecutive M elements of K row kb + i / 4 at
+      // column mb + 4 (i % 4), and lane j receives K rows kb..kb+3 of column mb + j.
+      constexpr bool kATrV = (KIND == kDweight);
+      constexpr bool kBTrV = (KIND == kDhidden || KIND == kDweight);
+      constexpr int kLPS = 8;  // load instructions per stage per wave (4 per operand)
+      const int nkv = (int)cdiv(K, 32);
+      const bool ktail = (K % 32) != 0;
+
+      // row-form: resources for tile rows [0,128) and [128,256); a wave loads one half only
+      __amdgpu_buffer_rsrc_t ra0, ra1, rb0, rb1;
+      uint32_t a_vo[4], b_vo[4];            // per load instruction: this lane's byte offset at k = 0
+      uint8_t a_ck[4], b_ck[4];             // row-form: this lane's logical K chunk per instruction
+      const char *a_tb = nullptr, *b_tb = nullptr;  // transposed: (k = 0, m = tile origin)
+      int64_t a_ldb = 0, b_ldb = 0;                 // transposed: bytes per K row
+
+      auto swz_row = [](int r) { return ((r >> 1) & 2) | (((r >> 1) & 1) ^ ((r >> 3) & 1)); };
+      const int swz_lane = swz_row(lane & 31);  // same for every fragment row of this lane
+      auto rsrc = [](const char *base, int64_t bytes) {
+        const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, (int)n, 0x00020000);
+      };
+      // Row-form source: rows of `ld_bytes` bytes; tile rows [0,128) start at base0
+      // with n0 valid rows, tile rows [128,256) at base1 with n1 valid rows.
+      auto setup_rows = [&](const char *base0, int64_t n0, const char *base1, int64_t n1,
+                            int64_t ld_bytes, __amdgpu_buffer_rsrc_t &r0, __amdgpu_buffer_rsrc_t &r1,
+                            uint32_t (&vo)[4],
+                            uint8_t (&ck)[4]) {
+        r0 = rsrc(base0, n0 * ld_bytes);
+        r1 = rsrc(base1, n1 * ld_bytes);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int row = 16 * (4 * wave + n) + (lane >> 2);  // tile row this lane loads
+          const int c = (lane & 3) ^ swz_row(row);
+          ck[n] = (uint8_t)c;
+          vo[n] = (uint32_t)((int64_t)(row & 127) * ld_bytes) + (uint32_t)(c * 16);
+        }
+      };
+      // Transposed source: element (k, m) at base + k * ld_bytes + m * 2, tile origin m0.
+      auto setup_tr = [&](int64_t m0, int64_t ld_bytes, uint32_t (&vo)[4]) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int krow = 8 * wave + 2 * n + (lane >> 5);
+          const int c = (lane & 31) ^ (4 * (krow & 3));
+          vo[n] = (uint32_t)((int64_t)krow * ld_bytes + m0 * 2 + c * 16);
+        }
+      };
+
+      if constexpr (KIND == kFwd) {
+        const int64_t v0 = mi * kTile, t0 = ni * kTile;
+        const int64_t ldb = a.H * 2;
+        const int64_t nv = a.V - v0, nt = a.T - t0;
+        setup_rows(Wp + v0 * ldb, nv < 128 ? nv : 128, Wp + (v0 + 128) * ldb, nv - 128,
+                   ldb, ra0, ra1, a_vo, a_ck);
+        setup_rows(hp + t0 * ldb, nt < 128 ? nt : 128, hp + (t0 + 128) * ldb, nt - 128,
+                   ldb, rb0, rb1, b_vo, b_ck);
+      } else if constexpr (KIND == kDlogits) {
+        const int64_t v0 = mi * kTile;
+        const int64_t ldb = a.H * 2;
+        const int64_t nv = a.Ws - v0;
+        setup_rows(Wp + (a.v_base + v0) * ldb, nv < 128 ? nv : 128,
+                   Wp + (a.v_base + v0 + 128) * ldb, nv - 128, ldb, ra0, ra1, a_vo, a_ck);
+        const int64_t e1 = 2 * ni + 1;
+        const int64_t tile0 = a.tile_list[2 * ni];
+        const int64_t tile1 = (e1 < a.n_skip_tiles) ? a.tile_list[e1] : -1;
+        const int64_t n0 = a.T - tile0 * kSkipTile;
+        const int64_t n1 = tile1 >= 0 ? a.T - tile1 * kSkipTile : 0;
+        setup_rows(hp + tile0 * kSkipTile * ldb, n0 < 128 ? n0 : 128,
+                   hp + (tile1 >= 0 ? tile1 : 0) * kSkipTile * ldb, n1 < 128 ? n1 : 128, ldb, rb0,
+                   rb1, b_vo, b_ck);
+      } else if constexpr (KIND == kDhidden) {
+        const int64_t ldb = (int64_t)a.ld_d * 2;
+        const int64_t nr = span_s1 - span_s0;
+        setup_rows(Dp + span_s0 * ldb, nr < 128 ? nr : 128, Dp + (span_s0 + 128) * ldb, nr - 128,
+                   ldb, ra0, ra1, a_vo, a_ck);
+        b_tb = Wp + a.v_base * a.H * 2;
+        b_ldb = a.H * 2;
+        setup_tr(ni * kTile, b_ldb, b_vo);
+      } else {
+        a_tb = Dp;
+        a_ldb = (int64_t)a.ld_d * 2;
+        setup_tr(mi * kTile, a_ldb, a_vo);
+        b_tb = hp;
+        b_ldb = a.H * 2;
+        setup_tr(ni * kTile, b_ldb, b_vo);
+      }
+
+      // Loads of stage s into ring buffer s % kNS, one operand at a time (4 instructions
+      // per wave each).  Stages past the last one are still issued, with zero-size
+      // descriptors (they read nothing and write zeros into a buffer nobody reads
+      // any more), so the loop body has no branch and the vmcnt targets are constant.
+      const __amdgpu_buffer_rsrc_t rnull = rsrc(Wp, 0);
+      auto issue_a = [&](int s) {
+        char *lb = smem + (s % kNS) * kStage;
+        const bool live = s < nkv;
+        if constexpr (kATrV) {
+          const __amdgpu_buffer_rsrc_t r =
+              live ? rsrc(a_tb + (int64_t)s * 32 * a_ldb, (K - (int64_t)s * 32) * a_ldb) : rnull;
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lb + (8 * wave + 2 * n) * 512, 16, a_vo[n], 0, 0, 0);
+        } else {
+          const __amdgpu_buffer_rsrc_t r = live ? ((wave >> 1) ? ra1 : ra0) : rnull;
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lb + (4 * wave + n) * 1024, 16, a_vo[n], s * 64, 0, 0);
+        }
+      };
+      auto issue_b = [&](int s) {
+        char *lbb = smem + (s % kNS) * kStage + kOpStage;
+        const bool live = s < nkv;
+        if constexpr (kBTrV) {
+          const __amdgpu_buffer_rsrc_t r =
+              live ? rsrc(b_tb + (int64_t)s * 32 * b_ldb, (K - (int64_t)s * 32) * b_ldb) : rnull;
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lbb + (8 * wave + 2 * n) * 512, 16, b_vo[n], 0, 0, 0);
+        } else {
+          const __amdgpu_buffer_rsrc_t r = live ? ((wave >> 1) ? rb1 : rb0) : rnull;
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lbb + (4 * wave + n) * 1024, 16, b_vo[n], s * 64, 0, 0);
+        }
+      };
+      // Last, partial K stage of a row-form operand: its chunks past K were read from
+      // the next row (or as zeros); overwrite them with zeros once this wave's loads
+      // of the stage have landed.
+      auto fix_tail = [&](int s) {
+        if (!(ktail && s == nkv - 1)) return;
+        char *lb = smem + (s % kNS) * kStage;
+        if constexpr (!kATrV) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            if ((int64_t)s * 32 + a_ck[n] * 8 >= K)
+              *reinterpret_cast<u32x4 *>(lb + (4 * wave + n) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (!kBTrV) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            if ((int64_t)s * 32 + b_ck[n] * 8 >= K)
+              *reinterpret_cast<u32x4 *>(lb + kOpStage + (4 * wave + n) * 1024 + lane * 16) =
+                  u32x4{0u, 0u, 0u, 0u};
+        }
+      };
+      // s_waitcnt immediates (gfx9): vmcnt in [3:0] and [15:14], expcnt [6:4] = 7 and
+      // lgkmcnt [11:8] = 15 (no wait on those)
+      constexpr int kVm16 = 0x0f70 | (16 & 15) | ((16 >> 4) << 14);  // <= 16 loads in flight
+      constexpr int kVm12 = 0x0f70 | (12 & 15) | ((12 >> 4) << 14);  // <= 12 loads in flight
+      constexpr int kLgkm0 = 0xc07f;                                 // lgkmcnt(0) only
+      static_assert(kNS == 4, "the vmcnt targets below assume a 4-stage ring");
+
+      // ---- fragment reads ----
+      const int G16 = lane >> 4, h16 = G16 & 1, g16 = G16 >> 1, li = lane & 15;
+      auto read_rowform = [&](const char *op, int wbase, int i, int q) -> u32x4 {
+        const int R = wbase + 32 * i + (lane & 31);
+        return *reinterpret_cast<const u32x4 *>(op + R * 64 + (((2 * q + g) ^ swz_lane) << 4));
+      };
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      auto read_tr = [&](const char *op, int wbase, int i, int q) -> u32x4 {
+        const int m = wbase + 32 * i + 16 * h16 + 4 * (li & 3);
+        const int sw = 4 * ((li >> 2) & 3);
+        const int col = ((((m >> 3) ^ sw)) << 4) + ((m & 7) << 1);
+        const int k0 = 16 * q + 8 * g16 + (li >> 2);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3))) *)(op + k0 * 512 + col));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 __attribute__((address_space(3))) *)(op + (k0 + 4) * 512 + col));
+        // 4 x b16 in two dwords, element 0 in the low half: already the fragment layout
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2.x, l2.y, h2.x, h2.y};
+      };
+      auto read_frags2 = [&](int s, int q, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+        const char *lb = smem + (s % kNS) * kStage;
+        auto ra_ = [&](int i) { return kATrV ? read_tr(lb, wm * 128, i, q) : read_rowform(lb, wm * 128, i, q); };
+        auto rb_ = [&](int j) {
+          return kBTrV ? read_tr(lb + kOpStage, wn * 128, j, q) : read_rowform(lb + kOpStage, wn * 128, j, q);
+        };
+        fa[0] = ra_(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = rb_(j);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) fa[i] = ra_(i);
+      };
+      constexpr int kReads = (kATrV ? 8 : 4) + (kBTrV ? 8 : 4);  // LDS reads per K slice
+      constexpr bool kAnyTr = kATrV || kBTrV;
+      constexpr int kVmemPerHalf = kAnyTr ? 8 : 4;  // loads spread over one half-stage
+      // 16 MFMAs of one K slice, with the next slice's LDS reads and (optionally) 4
+      // global->LDS loads spread between them
+      auto mma_slice = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], bool interleave, bool vmem) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
+        if (interleave) {
+#pragma unroll
+          for (int x = 0; x < kReads; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // one LDS read
+            if (vmem && x < kVmemPerHalf) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a load
+            __builtin_amdgcn_sched_group_barrier(0x008, kReads <= 8 ? 2 : 1, 0);   // MFMA(s)
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+
+      // ---- prologue: stages 0 .. kNS-2 in flight, stage 0 visible ----
+#pragma unroll
+      for (int s = 0; s < kNS - 1; ++s) {
+        issue_a(s);
+        issue_b(s);
+      }
+      __builtin_amdgcn_s_waitcnt(kVm16);  // this wave's stage-0 loads have landed
+      fix_tail(0);
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+      u32x4 F0a[4], F0b[4], F1a[4], F1b[4];
+      read_frags2(0, 0, F0a, F0b);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // Stages 0 .. nkv-2: each iteration also brings stage kt+1 into view and issues
+      // stage kt+3 (A half before the barrier, B half after it).  The last stage is
+      // peeled so the loop body is one straight MFMA path.
+      for (int kt = 0; kt + 1 < nkv; ++kt) {
+        // Row-form kernels spread the 8 loads of stage kt+3 over both halves (A before
+        // the barrier, B after it); the transposed-operand kernels are more latency
+        // bound and issue both halves before the barrier, spread over the first half.
+        issue_a(kt + kNS - 1);  // into the buffer stage kt-1 used
+        if constexpr (kAnyTr) issue_b(kt + kNS - 1);
+        read_frags2(kt, 1, F1a, F1b);
+        mma_slice(F0a, F0b, true, true);
+        // loads after stage kt+1's: A,B of stage kt+2 and A (and B) of stage kt+3
+        __builtin_amdgcn_s_waitcnt(kAnyTr ? kVm16 : kVm12);
+        fix_tail(kt + 1);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's reads of stage kt done
+        __builtin_amdgcn_s_barrier();
+        if constexpr (!kAnyTr) issue_b(kt + kNS - 1);
+        read_frags2(kt + 1, 0, F0a, F0b);
+        mma_slice(F1a, F1b, true, !kAnyTr);
+      }
+      read_frags2(nkv - 1, 1, F1a, F1b);
+      mma_slice(F0a, F0b, true, false);
+      mma_slice(F1a, F1b, false, false);
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // drain the trailing loads (they target free buffers)
+      __syncthreads();  // every wave is done with the ring before epilogues reuse LDS
     }
 
     // ---------------- epilogues ----------------
@@ -591,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int col = col0 + j * 32;
-            if (col < n_cols) prow[col] = a.first_split ? acc[i][j][r] : prow[col] + acc[i][j][r];
+            if (col < n_cols) prow[col] = acc[i][j][r];
           }
         }
     } else {

@@ -49,6 +49,8 @@ struct GemmArgs {
   void *D;                 // d-logits staging [T][ld_d]
   float *dh_acc;           // fp32 hidden-gradient accumulator [T][H]
   int32_t first_split;     // dH: 1 -> overwrite, 0 -> accumulate
+  int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
+                           // in flight on one XCD form a group_m x 32/group_m block)
   void *dW;                // [V][H]
 };
 

@@ -231,3 +231,95 @@ def test_kernel_addressing_full_workloads_sampled(cid):
     cfg = CONFIGS[cid]
     mask, _ = make_mask(cid, active_frac=0.5 if cid == 5 else None)
     model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2 if cfg.dtype == "bf16" else 4, mask, sample=True)
+
+
+# ---- bf16 path: LDS-direct buffer loads -------------------------------------------
+# Every global load of the bf16 kernels goes through a buffer descriptor, and the
+# hardware returns zeros for any byte at or past the descriptor's range, so memory
+# safety reduces to: each descriptor's [base, base + num_records) lies inside its
+# allocation.  LDS accesses must stay inside the ring (kNS stages of 32 KiB).
+
+NS, OPSTAGE = 4, 256 * 64
+
+
+def _rsrc(buf, base, nbytes, what):
+    n = 0 if nbytes <= 0 else min(nbytes, 0xFFFFFFFF)
+    if n == 0:
+        return
+    assert 0 <= base and base + n <= buf.n, f"{what}: descriptor [{base}, {base + n}) outside {buf.name} ({buf.n})"
+
+
+def model_bf16(T, H, V, S_split, mask, sample=False):
+    esz = 2
+    h = Buf("h", T * H * esz)
+    W = Buf("W", V * H * esz)
+    ld_max = cdiv(min(V, S_split), 8) * 8
+    D = Buf("D", T * ld_max * esz)
+    ldb = H * 2
+
+    def rows(buf, base0, n0, base1, n1, ld, what):
+        _rsrc(buf, base0, n0 * ld, what + " half0")
+        _rsrc(buf, base1, n1 * ld, what + " half1")
+
+    for mi, ni in itertools.product(_pick(cdiv(V, TILE), sample), _pick(cdiv(T, TILE), sample)):
+        v0, t0 = mi * TILE, ni * TILE
+        nv, nt = V - v0, T - t0
+        rows(W, v0 * ldb, min(nv, 128), (v0 + 128) * ldb, nv - 128, ldb, "fwd A")
+        rows(h, t0 * ldb, min(nt, 128), (t0 + 128) * ldb, nt - 128, ldb, "fwd B")
+    flags = S.tile_flags(mask, SKIP)
+    n_skip = len(flags)
+    tile_list = [i for i, f in enumerate(flags) if f] + [i for i, f in enumerate(flags) if not f]
+    n_act = sum(flags)
+    stiles = S.span_tiles(S.active_spans(mask, 128), SPAN_TILE)
+    for sp in _pick(cdiv(V, S_split), sample):
+        Ws = min(S_split, V - sp * S_split)
+        v_base = sp * S_split
+        ld_d = cdiv(Ws, 8) * 8
+        for mi in _pick(cdiv(ld_d, TILE), sample):
+            v0 = mi * TILE
+            nv = Ws - v0
+            rows(W, (v_base + v0) * ldb, min(nv, 128), (v_base + v0 + 128) * ldb, nv - 128, ldb, "dlg A")
+            for ni in _pick(cdiv(n_act, 2), sample):
+                t0 = tile_list[2 * ni]
+                t1 = tile_list[2 * ni + 1] if 2 * ni + 1 < n_skip else -1
+                n0 = T - t0 * SKIP
+                n1 = T - t1 * SKIP if t1 >= 0 else 0
+                rows(h, t0 * SKIP * ldb, min(n0, 128), max(t1, 0) * SKIP * ldb, min(n1, 128), ldb, "dlg B")
+        nk = cdiv(Ws, 32)
+        for (s0, s1) in [stiles[x] for x in _pick(len(stiles), sample)]:
+            nr = s1 - s0
+            rows(D, s0 * ld_d * 2, min(nr, 128), (s0 + 128) * ld_d * 2, nr - 128, ld_d * 2, "dh A")
+        for s in _pick(nk, sample):
+            _rsrc(W, (v_base + s * 32) * ldb, (Ws - s * 32) * ldb, f"dh B stage {s}")
+        nk = cdiv(T, 32)
+        for s in _pick(nk, sample):
+            _rsrc(D, s * 32 * ld_d * 2, (T - s * 32) * ld_d * 2, f"dw A stage {s}")
+            _rsrc(h, s * 32 * ldb, (T - s * 32) * ldb, f"dw B stage {s}")
+    # LDS: direct-load destinations and fragment reads stay inside one stage operand
+    for w, n, l in itertools.product(range(4), range(4), range(64)):
+        assert (4 * w + n) * 1024 + l * 16 + 16 <= OPSTAGE
+        assert (8 * w + 2 * n) * 512 + l * 16 + 16 <= OPSTAGE
+    for l in range(64):
+        li, g16, h16 = l & 15, l >> 5, (l >> 4) & 1
+        for q, i, wb in itertools.product(range(2), range(4), (0, 128)):
+            R = wb + 32 * i + (l & 31)
+            assert R * 64 + 64 <= OPSTAGE
+            m = wb + 32 * i + 16 * h16 + 4 * (li & 3)
+            col = (((m >> 3) ^ (4 * ((li >> 2) & 3))) << 4) + ((m & 7) << 1)
+            k0 = 16 * q + 8 * g16 + (li >> 2)
+            assert (k0 + 4) * 512 + col + 8 <= OPSTAGE
+
+
+@pytest.mark.parametrize("T,H,V,S_split", SHAPES)
+def test_bf16_descriptors_in_bounds(T, H, V, S_split):
+    rng = np.random.default_rng(T + 3 * V)
+    for mask in (np.ones(T, np.uint8), (rng.random(T) < 0.4).astype(np.uint8), np.zeros(T, np.uint8)):
+        model_bf16(T, H, V, S_split, mask)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_bf16_descriptors_full_workloads_sampled(cid):
+    from workloads import CONFIGS, make_mask
+    cfg = CONFIGS[cid]
+    mask, _ = make_mask(cid, active_frac=0.5 if cid == 5 else None)
+    model_bf16(cfg.T, cfg.H, cfg.V, cfg.vocab_split, mask, sample=True)
