@@ -26,11 +26,13 @@ enum KernelId : int32_t {
   kIdDhidden,
   kIdDweight,
   kIdFinalize,
+  kIdTranspose,
   kIdCount
 };
 const char *const kKernelNames[kIdCount] = {
     "spans_build", "fwd_logits_softmax", "fwd_combine", "bwd_lists",
-    "dlogits",     "dhidden_spans",      "dweight",     "dhidden_finalize"};
+    "dlogits",     "dhidden_spans",      "dweight",     "dhidden_finalize",
+    "transpose"};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -50,12 +52,15 @@ int32_t split_or_default(int32_t s) { return s == 0 ? kDefaultSplit : s; }
 size_t fwd_bytes(int64_t T, int64_t V) { return (size_t)cdiv(V, kTile) * (size_t)T * 16; }
 
 struct BwdLayout {
-  size_t counts, tile_list, span_tiles, D, acc, total;
-  int64_t span_tile_cap;
+  size_t counts, tile_list, span_tiles, D, Dt, Wt, ht, acc, total;
+  int64_t span_tile_cap, ld_wt, ld_t;
 };
 
 // Backward workspace: [counts | token-tile list | span-tile list | d-logits
-// staging sized by the widest live split | fp32 dH accumulator].
+// staging [T][ld] sized by the widest live split | the same transposed, [W][ld_t] |
+// W^T [H][ld_wt] | h^T [H][ld_t] | fp32 dH accumulator].  The transposed copies put
+// the contraction index of the hidden- and weight-gradient products in contiguous
+// memory, so every contraction streams K-contiguous rows.
 BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   BwdLayout L{};
   const int64_t per = 16 / elt_size(dt);
@@ -64,6 +69,9 @@ BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   L.span_tile_cap = cdiv(T, kSpanTile) + (T + 1) / 2 + 1;
   const int64_t w_max = V < S ? V : S;
   const int64_t ld_max = cdiv(w_max, per) * per;
+  L.ld_wt = cdiv(V, per) * per;
+  L.ld_t = cdiv(T, per) * per;
+  const size_t esz = (size_t)elt_size(dt);
   size_t off = 0;
   L.counts = off;
   off = align_up(off + 64, 256);
@@ -72,7 +80,13 @@ BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   L.span_tiles = off;
   off = align_up(off + (size_t)L.span_tile_cap * 8, 256);
   L.D = off;
-  off = align_up(off + (size_t)T * (size_t)ld_max * (size_t)elt_size(dt), 256);
+  off = align_up(off + (size_t)T * (size_t)ld_max * esz, 256);
+  L.Dt = off;
+  off = align_up(off + (size_t)w_max * (size_t)L.ld_t * esz, 256);
+  L.Wt = off;
+  off = align_up(off + (size_t)H * (size_t)L.ld_wt * esz, 256);
+  L.ht = off;
+  off = align_up(off + (size_t)H * (size_t)L.ld_t * esz, 256);
   L.acc = off;
   off = align_up(off + (size_t)T * (size_t)H * 4, 256);
   L.total = off;
@@ -256,6 +270,11 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
   a.span_tiles = reinterpret_cast<int32_t *>(base + L.span_tiles);
   a.n_skip_tiles = (int32_t)cdiv(T, kSkipTile);
   a.D = base + L.D;
+  a.Dt = base + L.Dt;
+  a.Wt = base + L.Wt;
+  a.ht = base + L.ht;
+  a.ld_wt = L.ld_wt;
+  a.ld_t = L.ld_t;
   a.dh_acc = reinterpret_cast<float *>(base + L.acc);
   a.dW = d_weight;
 
@@ -265,6 +284,14 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
                         reinterpret_cast<int32_t *>(base + L.tile_list),
                         reinterpret_cast<int32_t *>(base + L.counts),
                         reinterpret_cast<int32_t *>(base + L.span_tiles), L.span_tile_cap, st);
+  });
+  if (s != FLH_OK) return s;
+  s = run(kIdTranspose, -1, st, [&] {
+    return launch_transpose((int)elt_size(dt), W, V, H, base + L.Wt, L.ld_wt, st);
+  });
+  if (s != FLH_OK) return s;
+  s = run(kIdTranspose, -1, st, [&] {
+    return launch_transpose((int)elt_size(dt), h, T, H, base + L.ht, L.ld_t, st);
   });
   if (s != FLH_OK) return s;
 

@@ -337,3 +337,80 @@ hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, co
 }
 
 }  // namespace flh
+
+// ---------------------------------------------------------------------------------
+// Transpose through LDS: out[c][r] = in[r][c] (in [R][C], out [C][ld_out]), zeros in
+// the padding columns r in [R, ld_out).  A workgroup moves 64 x 64 tiles with
+// 16-byte loads and stores, walking the tile grid with a stride of the launch size.
+// The backward uses it to lay W and h out with the contraction index contiguous
+// for the hidden- and weight-gradient products.
+namespace flh {
+namespace {
+
+constexpr int kTrTile = 64;
+
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, int64_t R, int64_t C,
+                                                        E *__restrict__ out, int64_t ld_out,
+                                                        int64_t c_tiles, int64_t n_tiles) {
+  constexpr int kT = kTrTile;
+  constexpr int kV = 16 / sizeof(E);  // elements per 16-byte vector
+  constexpr int kVecRow = kT / kV;    // vectors per tile row
+  __shared__ E tile[kT][kT + kV];     // padded rows
+  const int tid = threadIdx.x;
+  for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int64_t r0 = (t / c_tiles) * kT, c0 = (t % c_tiles) * kT;
+    for (int idx = tid; idx < kT * kVecRow; idx += 256) {
+      const int rr = idx / kVecRow, cv = (idx % kVecRow) * kV;
+      const int64_t r = r0 + rr, c = c0 + cv;
+      E v[kV];
+      if (r < R && c + kV <= C) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(in + r * C + c);
+        __builtin_memcpy(v, &x, 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kV; ++e) v[e] = (r < R && c + e < C) ? in[r * C + c + e] : E(0);
+      }
+#pragma unroll
+      for (int e = 0; e < kV; ++e) tile[rr][cv + e] = v[e];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kT * kVecRow; idx += 256) {
+      const int cc = idx / kVecRow, rv = (idx % kVecRow) * kV;
+      const int64_t c = c0 + cc, r = r0 + rv;
+      if (c >= C || r >= ld_out) continue;
+      E v[kV];
+#pragma unroll
+      for (int e = 0; e < kV; ++e) v[e] = (r + e < R) ? tile[rv + e][cc] : E(0);
+      if (r + kV <= ld_out) {
+        uint4 x;
+        __builtin_memcpy(&x, v, 16);
+        *reinterpret_cast<uint4 *>(out + c * ld_out + r) = x;
+      } else {
+        for (int e = 0; e < kV && r + e < ld_out; ++e) out[c * ld_out + r + e] = v[e];
+      }
+    }
+    __syncthreads();  // the tile is refilled by the next iteration
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
+                            hipStream_t st) {
+  const int64_t c_tiles = (C + kTrTile - 1) / kTrTile;
+  const int64_t n_tiles = c_tiles * ((ld_out + kTrTile - 1) / kTrTile);
+  if (n_tiles <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)(n_tiles < (1 << 20) ? n_tiles : (1 << 20));
+  if (esz == 2)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t *>(in), R, C, reinterpret_cast<uint16_t *>(out),
+                       ld_out, c_tiles, n_tiles);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, dim3(grid), dim3(256), 0, st,
+                       reinterpret_cast<const float *>(in), R, C, reinterpret_cast<float *>(out), ld_out,
+                       c_tiles, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace flh

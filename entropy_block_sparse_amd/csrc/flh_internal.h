@@ -19,8 +19,8 @@ constexpr int kSpanTile = 256;
 enum GemmKind : int {
   kFwd = 0,   // z = W h^T tile + online softmax partials          (K = H)
   kDlogits,   // recompute z over active token tiles -> d-logits  (K = H)
-  kDhidden,   // dH[span rows] (+)= D[span rows, :] W_s           (K = W_s)
-  kDweight,   // dW[split rows] = D^T h                          (K = T)
+  kDhidden,   // dH[span rows] (+)= D[span rows, :] W_s           (K = W_s; B = W^T rows)
+  kDweight,   // dW[split rows] = D^T h                          (K = T; A = D^T rows, B = h^T rows)
 };
 
 // Everything a contraction kernel needs; plain data, passed by value.
@@ -47,6 +47,11 @@ struct GemmArgs {
   // outputs / staging
   float *part;             // forward partials [ceil(V/256)][T][4]
   void *D;                 // d-logits staging [T][ld_d]
+  void *Dt;                // the same d-logits transposed: [W_s][ld_t]
+  const void *Wt;          // W transposed: [H][ld_wt]
+  const void *ht;          // h transposed: [H][ld_t]
+  int64_t ld_wt;           // row stride (elements) of Wt: V rounded up to 16 bytes
+  int64_t ld_t;            // row stride (elements) of ht and Dt: T rounded up to 16 bytes
   float *dh_acc;           // fp32 hidden-gradient accumulator [T][H]
   int32_t first_split;     // dH: 1 -> overwrite, 0 -> accumulate
   int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
@@ -68,6 +73,11 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
 
 hipError_t launch_combine(int64_t T, int64_t V, const float *part, const int64_t *targets,
                           float *logprob, float *entropy, float *lse, hipStream_t st);
+
+// out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for R <= r < ld_out.
+// in: [R][C] row-major; out: [C][ld_out]; elements of esz bytes (2 or 4).
+hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
+                            hipStream_t st);
 
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc,
                            const uint8_t *mask, void *dh, hipStream_t st);

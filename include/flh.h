@@ -121,6 +121,12 @@ int64_t flh_span_capacity(int64_t T, int32_t max_gap);
 /*
  * Workspace bytes the call `op` needs for these sizes (0 for FLH_OP_SPANS).
  * vocab_split 0 means 16384.  Returns 0 for invalid sizes as well.
+ * Forward: per-tile softmax partials, ceil(V/256) * T * 16 bytes.
+ * Backward: work lists; the d-logits staging of the widest split in two layouts
+ * (token-major T x W and vocabulary-major W x T, W = min(V, vocab_split)); W and h
+ * transposed (H x V and H x T, so that every contraction reads its contraction
+ * index contiguously); and an fp32 T x H hidden-gradient accumulator.  For
+ * T = 16384, H = 4096, V = 128256 in bf16 this is about 2.5 GB.
  */
 size_t flh_workspace_bytes(flh_op op, flh_dtype dt, int64_t T, int64_t H, int64_t V,
                            int32_t vocab_split);
