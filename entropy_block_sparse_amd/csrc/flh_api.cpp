@@ -49,6 +49,16 @@ bool dims_ok(flh_dtype dt, int64_t T, int64_t H, int64_t V) {
 
 int32_t split_or_default(int32_t s) { return s == 0 ? kDefaultSplit : s; }
 
+// Row stride (elements) for a workspace matrix with n columns: a multiple of 64
+// elements that is odd, so consecutive rows start an odd number of 128-byte lines
+// apart (bf16) and the rows a load instruction touches spread over the memory
+// channels instead of repeating one power-of-two stride.
+int64_t pad_ld(int64_t n) {
+  int64_t ld = cdiv(n, 64) * 64;
+  if ((ld / 64) % 2 == 0) ld += 64;
+  return ld;
+}
+
 size_t fwd_bytes(int64_t T, int64_t V) { return (size_t)cdiv(V, kTile) * (size_t)T * 16; }
 
 struct BwdLayout {
@@ -58,19 +68,18 @@ struct BwdLayout {
 
 // Backward workspace: [counts | token-tile list | span-tile list | d-logits
 // staging [T][ld] sized by the widest live split | the same transposed, [W][ld_t] |
-// W^T [H][ld_wt] | h^T [H][ld_t] | fp32 dH accumulator].  The transposed copies put
+// W^T per split [splits][H][ld_wt] | h^T [H][ld_t] | fp32 dH accumulator].  The transposed copies put
 // the contraction index of the hidden- and weight-gradient products in contiguous
 // memory, so every contraction streams K-contiguous rows.
 BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   BwdLayout L{};
-  const int64_t per = 16 / elt_size(dt);
   const int64_t n_skip = cdiv(T, kSkipTile);
   // every span holds >= 1 token and spans are >= 1 token apart: <= ceil(T/2) spans
   L.span_tile_cap = cdiv(T, kSpanTile) + (T + 1) / 2 + 1;
   const int64_t w_max = V < S ? V : S;
-  const int64_t ld_max = cdiv(w_max, per) * per;
-  L.ld_wt = cdiv(V, per) * per;
-  L.ld_t = cdiv(T, per) * per;
+  const int64_t ld_max = pad_ld(w_max);
+  L.ld_wt = pad_ld(w_max);
+  L.ld_t = pad_ld(T);
   const size_t esz = (size_t)elt_size(dt);
   size_t off = 0;
   L.counts = off;
@@ -84,7 +93,7 @@ BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   L.Dt = off;
   off = align_up(off + (size_t)w_max * (size_t)L.ld_t * esz, 256);
   L.Wt = off;
-  off = align_up(off + (size_t)H * (size_t)L.ld_wt * esz, 256);
+  off = align_up(off + (size_t)cdiv(V, S) * (size_t)H * (size_t)L.ld_wt * esz, 256);
   L.ht = off;
   off = align_up(off + (size_t)H * (size_t)L.ld_t * esz, 256);
   L.acc = off;
@@ -251,7 +260,6 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
   if (cus <= 0) return FLH_E_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char *base = reinterpret_cast<char *>(ws);
-  const int64_t per = 16 / elt_size(dt);
 
   GemmArgs a{};
   a.T = T;
@@ -287,11 +295,11 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
   });
   if (s != FLH_OK) return s;
   s = run(kIdTranspose, -1, st, [&] {
-    return launch_transpose((int)elt_size(dt), W, V, H, base + L.Wt, L.ld_wt, st);
+    return launch_transpose((int)elt_size(dt), W, V, H, base + L.Wt, L.ld_wt, S, st);
   });
   if (s != FLH_OK) return s;
   s = run(kIdTranspose, -1, st, [&] {
-    return launch_transpose((int)elt_size(dt), h, T, H, base + L.ht, L.ld_t, st);
+    return launch_transpose((int)elt_size(dt), h, T, H, base + L.ht, L.ld_t, 0, st);
   });
   if (s != FLH_OK) return s;
 
@@ -303,10 +311,11 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
     const int64_t Ws = (V - sp * S) < S ? (V - sp * S) : S;
     a.v_base = sp * S;
     a.Ws = (int32_t)Ws;
-    a.ld_d = (int32_t)(cdiv(Ws, per) * per);
+    a.ld_d = (int32_t)pad_ld(Ws);
     a.first_split = sp == 0;
+    a.Wt = base + L.Wt + (size_t)sp * (size_t)H * (size_t)L.ld_wt * (size_t)elt_size(dt);
     const int32_t tag = (int32_t)sp;
-    const int64_t v_tiles = cdiv(a.ld_d, kTile);
+    const int64_t v_tiles = cdiv(Ws, kTile);
     s = run(kIdDlogits, tag, st, [&] {
       return launch_gemm((int)dt, kDlogits, a, grid_for(v_tiles * cdiv(a.n_skip_tiles, 2), cus), st);
     });

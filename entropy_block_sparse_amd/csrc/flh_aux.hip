@@ -339,11 +339,13 @@ hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, co
 }  // namespace flh
 
 // ---------------------------------------------------------------------------------
-// Transpose through LDS: out[c][r] = in[r][c] (in [R][C], out [C][ld_out]), zeros in
-// the padding columns r in [R, ld_out).  A workgroup moves 64 x 64 tiles with
-// 16-byte loads and stores, walking the tile grid with a stride of the launch size.
-// The backward uses it to lay W and h out with the contraction index contiguous
-// for the hidden- and weight-gradient products.
+// Blocked transpose through LDS: rows of `in` ([R][C]) are taken in blocks of `block`
+// rows; block b becomes out_b = out + b * C * ld_out, [C][ld_out], with
+// out_b[c][r] = in[b * block + r][c] and zeros in the padding columns past the
+// block's rows.  A workgroup moves 64 x 64 tiles with 16-byte loads and stores,
+// walking the tile grid with a stride of the launch size.  The backward uses it to
+// lay W (one block per vocabulary split) and h out with the contraction index
+// contiguous for the hidden- and weight-gradient products.
 namespace flh {
 namespace {
 
@@ -351,25 +353,32 @@ constexpr int kTrTile = 64;
 
 template <typename E>
 __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, int64_t R, int64_t C,
-                                                        E *__restrict__ out, int64_t ld_out,
-                                                        int64_t c_tiles, int64_t n_tiles) {
+                                                        E *__restrict__ out, int64_t ld_out, int64_t block,
+                                                        int64_t c_tiles, int64_t r_tiles, int64_t n_tiles) {
   constexpr int kT = kTrTile;
   constexpr int kV = 16 / sizeof(E);  // elements per 16-byte vector
   constexpr int kVecRow = kT / kV;    // vectors per tile row
   __shared__ E tile[kT][kT + kV];     // padded rows
   const int tid = threadIdx.x;
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int64_t r0 = (t / c_tiles) * kT, c0 = (t % c_tiles) * kT;
+    // tile (blk, rt, ct): rows blk * block + rt * 64 .., columns ct * 64 ..
+    const int64_t blk = t / (r_tiles * c_tiles);
+    const int64_t rem = t - blk * r_tiles * c_tiles;
+    const int64_t rb = (rem / c_tiles) * kT, c0 = (rem % c_tiles) * kT;  // block-local row
+    const int64_t r0 = blk * block + rb;                                   // row of `in`
+    const int64_t R_blk = (R - blk * block) < block ? (R - blk * block) : block;
+    E *outb = out + blk * C * ld_out;
     for (int idx = tid; idx < kT * kVecRow; idx += 256) {
       const int rr = idx / kVecRow, cv = (idx % kVecRow) * kV;
       const int64_t r = r0 + rr, c = c0 + cv;
+      const bool live = rb + rr < R_blk;  // a row of this block (rows past it read as 0)
       E v[kV];
-      if (r < R && c + kV <= C) {
+      if (live && c + kV <= C) {
         const uint4 x = *reinterpret_cast<const uint4 *>(in + r * C + c);
         __builtin_memcpy(v, &x, 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < kV; ++e) v[e] = (r < R && c + e < C) ? in[r * C + c + e] : E(0);
+        for (int e = 0; e < kV; ++e) v[e] = (live && c + e < C) ? in[r * C + c + e] : E(0);
       }
 #pragma unroll
       for (int e = 0; e < kV; ++e) tile[rr][cv + e] = v[e];
@@ -377,17 +386,17 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
     __syncthreads();
     for (int idx = tid; idx < kT * kVecRow; idx += 256) {
       const int cc = idx / kVecRow, rv = (idx % kVecRow) * kV;
-      const int64_t c = c0 + cc, r = r0 + rv;
+      const int64_t c = c0 + cc, r = rb + rv;  // block-local output column
       if (c >= C || r >= ld_out) continue;
       E v[kV];
 #pragma unroll
-      for (int e = 0; e < kV; ++e) v[e] = (r + e < R) ? tile[rv + e][cc] : E(0);
+      for (int e = 0; e < kV; ++e) v[e] = (r + e < R_blk) ? tile[rv + e][cc] : E(0);
       if (r + kV <= ld_out) {
         uint4 x;
         __builtin_memcpy(&x, v, 16);
-        *reinterpret_cast<uint4 *>(out + c * ld_out + r) = x;
+        *reinterpret_cast<uint4 *>(outb + c * ld_out + r) = x;
       } else {
-        for (int e = 0; e < kV && r + e < ld_out; ++e) out[c * ld_out + r + e] = v[e];
+        for (int e = 0; e < kV && r + e < ld_out; ++e) outb[c * ld_out + r + e] = v[e];
       }
     }
     __syncthreads();  // the tile is refilled by the next iteration
@@ -397,19 +406,23 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
 }  // namespace
 
 hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
-                            hipStream_t st) {
+                            int64_t block, hipStream_t st) {
+  if (block <= 0) block = R;
+  if (block % kTrTile != 0 && block != R) return hipErrorInvalidValue;
   const int64_t c_tiles = (C + kTrTile - 1) / kTrTile;
-  const int64_t n_tiles = c_tiles * ((ld_out + kTrTile - 1) / kTrTile);
+  const int64_t r_tiles = (ld_out + kTrTile - 1) / kTrTile;  // per block
+  const int64_t n_blocks = (R + block - 1) / block;
+  const int64_t n_tiles = n_blocks * r_tiles * c_tiles;
   if (n_tiles <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(n_tiles < (1 << 20) ? n_tiles : (1 << 20));
   if (esz == 2)
     hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t *>(in), R, C, reinterpret_cast<uint16_t *>(out),
-                       ld_out, c_tiles, n_tiles);
+                       ld_out, block, c_tiles, r_tiles, n_tiles);
   else
     hipLaunchKernelGGL(transpose_kernel<float>, dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const float *>(in), R, C, reinterpret_cast<float *>(out), ld_out,
-                       c_tiles, n_tiles);
+                       block, c_tiles, r_tiles, n_tiles);
   return hipGetLastError();
 }
 

@@ -49,15 +49,23 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = 144;
 constexpr int kOpBytes = kTile * kRowBytes;  // one operand tile, one stage
 constexpr int kLdsBytes = 4 * kOpBytes;      // A and B, two stages (147456 B)
-// bf16 path: a ring of kNS stages of 32 K elements (64 bytes per row) per operand
-constexpr int kNS = 4;
-constexpr int kOpStage = kTile * 64;       // one operand, one stage: 16 KiB
-constexpr int kStage = 2 * kOpStage;       // 32 KiB
-constexpr int kLdsBytesV2 = kNS * kStage;  // 128 KiB
+// bf16 path: two stages of 64 K elements (128 bytes per row) per operand
+constexpr int kOpStage = kTile * 128;     // one operand, one stage: 32 KiB
+constexpr int kStage = 2 * kOpStage;      // 64 KiB
+constexpr int kLdsBytesV2 = 2 * kStage;   // 128 KiB
 // bf16 d-logits epilogue: the 256 x 256 tile staged token-major in LDS, rows padded to
 // 528 bytes (16-byte aligned, consecutive rows 4 banks apart)
 constexpr int kLsPitch = 528;
 constexpr int kLdsBytesDlg = kTile * kLsPitch > kLdsBytesV2 ? kTile * kLsPitch : kLdsBytesV2;
+// (the bf16 hidden-gradient epilogue stages half a tile of fp32, 128 KiB, in the ring)
+
+// Shared memory of one kernel instantiation: the main loop's stages plus whatever its
+// epilogue stages.
+template <typename T, int KIND>
+constexpr int lds_bytes() {
+  return sizeof(T) != 2 ? kLdsBytes
+                        : (KIND == kDlogits || KIND == kDweight ? kLdsBytesDlg : kLdsBytesV2);
+}
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <typename T> struct Elt;
@@ -158,8 +166,7 @@ template <typename T, int KIND>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
     const GemmArgs a) {
   constexpr bool kV2 = sizeof(T) == 2;  // bf16: LDS-direct ring; fp32: register-staged
-  __shared__ __attribute__((aligned(16))) char
-      smem[kV2 ? (KIND == kDlogits ? kLdsBytesDlg : kLdsBytesV2) : kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[lds_bytes<T, KIND>()];
   constexpr int kPer = Elt<T>::kPer;    // elements per 16-byte chunk
   constexpr int64_t kEsz = sizeof(T);
 
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     n_tiles = cdiv(a.T, kTile);
     K = a.H;
   } else if constexpr (KIND == kDlogits) {
-    m_tiles = cdiv(a.ld_d, kTile);
+    m_tiles = cdiv(a.Ws, kTile);
     n_pairs_gemm = cdiv(uni(a.counts[0]), 2);
     n_pairs_all = cdiv(a.n_skip_tiles, 2);
     n_tiles = n_pairs_gemm;
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int64_t n_items =
       n_gemm + (KIND == kDlogits ? m_tiles * (n_pairs_all - n_pairs_gemm) : 0);
   const int64_t G = gridDim.x;
-  const int64_t remap_end = (G % 8 == 0) ? (n_gemm / G) * G : 0;
+  const bool remap = (G % 8) == 0;
 
   const char *hp = reinterpret_cast<const char *>(a.h);
   const char *Wp = reinterpret_cast<const char *>(a.W);
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t mi = z % m_tiles;
         const int64_t p = n_pairs_gemm + z / m_tiles;
         const int64_t c0 = mi * kTile;
-        const int64_t c1 = imin(c0 + kTile, a.ld_d);
+        const int64_t c1 = imin(c0 + kTile, cdiv(a.Ws, kPer) * kPer);
         // token-major staging: rows of the pair's tokens, columns [c0, c1)
         constexpr int kChunks = kTile / kPer;
         char *Dw = const_cast<char *>(Dp);
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             *reinterpret_cast<u32x4 *>(Dw + (t * a.ld_d + col) * kEsz) = u32x4{0u, 0u, 0u, 0u};
         }
         // vocabulary-major staging: rows v in [c0, min(c0 + 256, Ws)), the pair's
-        // tokens including the zero padding up to ld_t
+        // tokens including the zero padding up to a whole 16-byte chunk
         const int64_t v1 = imin(c0 + kTile, (int64_t)a.Ws);
         constexpr int kVecTile = kSkipTile / kPer;  // 16-byte vectors per token tile
         char *Dtw = reinterpret_cast<char *>(a.Dt);
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const int64_t v = c0 + vr;
           if (e >= a.n_skip_tiles || v >= v1) continue;
           const int64_t t = (int64_t)a.tile_list[e] * kSkipTile + vec * kPer;
-          if (t < a.ld_t)
+          if (t < cdiv(a.T, kPer) * kPer)
             *reinterpret_cast<u32x4 *>(Dtw + (v * a.ld_t + t) * kEsz) = u32x4{0u, 0u, 0u, 0u};
         }
         continue;
@@ -245,11 +252,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
 
     // ---------------- tile coordinates ----------------
+    // Workgroups are dealt to the 8 XCDs round-robin (XCD = id mod 8).  Within each
+    // round of G tiles, give the workgroups of XCD x a contiguous run of tile ids, so
+    // the tiles resident on one XCD form a compact block sharing operand rows in its
+    // L2.  The last round may be partial: its n_round tiles are split the same way.
     int64_t L = item;
-    if (item < remap_end) {
+    if (remap) {
       const int64_t r = item / G;
       const int64_t b = item - r * G;
-      L = r * G + (b & 7) * (G >> 3) + (b >> 3);
+      const int64_t n_round = imin(G, n_gemm - r * G);
+      const int64_t x = b & 7, q = n_round >> 3, rem8 = n_round & 7;
+      L = r * G + x * q + imin(x, rem8) + (b >> 3);
     }
     int64_t mi, ni;
     group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : 8, mi, ni);
@@ -279,10 +292,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     } else if constexpr (KIND == kDhidden) {
       const int64_t ldb = (int64_t)a.ld_d * kEsz, nr = span_s1 - span_s0;
       srcA = RowSrc{Dp + span_s0 * ldb, Dp + (span_s0 + 128) * ldb, imin(nr, 128), nr - 128, ldb, 0};
-      // W^T rows n (hidden units), from element v_base (the split's first row of W)
+      // rows n (hidden units) of this split's block of W^T
       const int64_t n0 = ni * kTile, ldw = a.ld_wt * kEsz;
-      const char *wt = reinterpret_cast<const char *>(a.Wt) + n0 * ldw + a.v_base * kEsz;
-      srcB = RowSrc{wt, wt + 128 * ldw, imin(a.H - n0, 128), a.H - n0 - 128, ldw, a.v_base * kEsz};
+      const char *wt = reinterpret_cast<const char *>(a.Wt) + n0 * ldw;
+      srcB = RowSrc{wt, wt + 128 * ldw, imin(a.H - n0, 128), a.H - n0 - 128, ldw, 0};
     } else {
       // vocabulary-major staging rows v and h^T rows n, both over all tokens
       const int64_t v0 = mi * kTile, n0 = ni * kTile, ldt = a.ld_t * kEsz;
@@ -299,9 +312,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    if constexpr (KIND == kDhidden) {
-      // Splits after the first continue the fp32 sum of the earlier splits: start the
-      // accumulators from it, so the epilogue is a plain store.
+    if constexpr (KIND == kDhidden && !kV2) {
+      // fp32: splits after the first continue the fp32 sum of the earlier splits: start
+      // the accumulators from it, so the epilogue is a plain store.  (The bf16 epilogue
+      // adds the earlier sum while it stores.)
       if (!a.first_split) {
         const int n_rows = (int)(span_s1 - span_s0);
         const int64_t n_tile = ni * kTile;
@@ -405,145 +419,143 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         __syncthreads();
       }
     } else {
-      // ================= bf16: LDS-direct loads into a kNS-stage ring =================
-      // A stage holds 32 K elements of both operands, [256 rows][4 chunks of 16 B] per
-      // operand; logical chunk c of row r sits at position c ^ swz_row(r), which
-      // spreads the 16 rows read together by a fragment read over distinct banks.
-      // Loads go straight from global memory into LDS (lane l of a wave writes 16
-      // bytes at the instruction's LDS base + 16 l), kNS-1 stages ahead of the MFMAs;
-      // no VGPRs stage the data and no LDS stores are issued.
-      const int nkv = (int)cdiv(K, 32);
-      const bool ktail = (K % 32) != 0;
-      auto swz_row = [](int r) { return ((r >> 1) & 2) | (((r >> 1) & 1) ^ ((r >> 3) & 1)); };
-      const int swz_lane = swz_row(lane & 31);  // same for every fragment row of this lane
+      // ============ bf16: LDS-direct loads, double-buffered 64-element K stages ============
+      // A stage holds 64 K elements (128 bytes) of each of the 256 tile rows of both
+      // operands, [256 rows][8 chunks of 16 B] per operand; logical chunk c of row r
+      // sits at position c ^ ((r >> 1) & 7), so the 16 rows that a fragment read
+      // touches together fall on distinct banks.  A load instruction fetches whole
+      // 128-byte row segments (8 lanes per row), which the cache serves with one
+      // request per row -- half the requests of 64-byte segments.  Loads go straight
+      // from global memory into LDS (lane l writes 16 bytes at the instruction's LDS
+      // base + 16 l), no VGPRs stage the data; stage kt+1 streams into the other
+      // buffer while stage kt is multiplied.
+      constexpr int kBKv = 64;
+      const int nkv = (int)cdiv(K, kBKv);
+      const bool ktail = (K % kBKv) != 0;
+      auto swz = [](int r) { return (r >> 1) & 7; };
+      const int swz_lane = swz(lane & 31);  // same for every fragment row of this lane
       auto rsrc = [](const char *base, int64_t bytes) {
         const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, (int)n, 0x00020000);
       };
-      // Wave w loads tile rows [64 w, 64 w + 64): waves 0, 1 from half 0, waves 2, 3
-      // from half 1; load instruction k covers rows 16 (4 w + k) .. + 15, four lanes
-      // per row.
+      // Wave w loads tile rows [64 w, 64 w + 64) (waves 0, 1 from half 0, waves 2, 3
+      // from half 1); its load instruction k (0..7) covers rows 64 w + 8 k .. + 7.
+      auto load_row = [&](int k) { return 64 * wave + 8 * k + (lane >> 3); };
+      auto load_chunk = [&](int k) { return (lane & 7) ^ swz(load_row(k)); };
       __amdgpu_buffer_rsrc_t ra, rb;
-      uint32_t a_vo[4], b_vo[4];  // per load instruction: this lane's byte offset at k = 0
-      uint8_t a_ck[4], b_ck[4];   // this lane's logical K chunk per instruction
-      auto setup = [&](const RowSrc &s, __amdgpu_buffer_rsrc_t &r, uint32_t (&vo)[4], uint8_t (&ck)[4]) {
+      uint32_t a_vo[8], b_vo[8];  // per load instruction: this lane's byte offset at k = 0
+      auto setup = [&](const RowSrc &s, __amdgpu_buffer_rsrc_t &r, uint32_t (&vo)[8]) {
         const bool h1 = (wave >> 1) != 0;
         const int64_t n = h1 ? s.n1 : s.n0;
         r = rsrc(uni(h1 ? s.base1 : s.base0), uni(n > 0 ? n * s.ldb - s.trim : 0));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int row = 16 * (4 * wave + k) + (lane >> 2);
-          const int c = (lane & 3) ^ swz_row(row);
-          ck[k] = (uint8_t)c;
-          vo[k] = (uint32_t)((int64_t)(row & 127) * s.ldb) + (uint32_t)(c * 16);
-        }
+        for (int k = 0; k < 8; ++k)
+          vo[k] = (uint32_t)((int64_t)(load_row(k) & 127) * s.ldb) + (uint32_t)(load_chunk(k) * 16);
       };
-      setup(srcA, ra, a_vo, a_ck);
-      setup(srcB, rb, b_vo, b_ck);
-      // Loads of stage s into ring buffer s % kNS, one operand at a time.  Stages past
-      // the last one are still issued, with a zero-size descriptor (they read nothing
-      // and write zeros into a buffer nobody reads any more), so the loop body has no
-      // branch and the vmcnt targets are constant.
-      const __amdgpu_buffer_rsrc_t rnull = rsrc(Wp, 0);
-      auto issue = [&](int s, const __amdgpu_buffer_rsrc_t &r, const uint32_t (&vo)[4], int op) {
-        char *lb = smem + (s % kNS) * kStage + op * kOpStage;
-        const __amdgpu_buffer_rsrc_t rr = s < nkv ? r : rnull;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, lb + (4 * wave + k) * 1024, 16, vo[k], s * 64, 0, 0);
+      setup(srcA, ra, a_vo);
+      setup(srcB, rb, b_vo);
+      // load k (0..7) of operand op (0 = A, 1 = B) of stage s
+      auto issue_one = [&](int s, int op, int k) {
+        char *lb = smem + (s & 1) * kStage + op * kOpStage + (8 * wave + k) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, lb, 16, op ? b_vo[k] : a_vo[k], s * 128, 0, 0);
       };
-      auto issue_a = [&](int s) { issue(s, ra, a_vo, 0); };
-      auto issue_b = [&](int s) { issue(s, rb, b_vo, 1); };
       // Last, partial K stage: chunks wholly past K were read from the next row (or
       // as zeros); overwrite them with zeros once this wave's loads of the stage have
       // landed.  A chunk that straddles K is kept: past K it holds the zero padding
-      // of the token-major staging, the next rows of W^T (multiplied by that zero
-      // padding), or the zero padding of h^T and of the vocabulary-major staging.
+      // of the token-major staging, of the split's block of W^T, of h^T or of the
+      // vocabulary-major staging.
       auto fix_tail = [&](int s) {
         if (!(ktail && s == nkv - 1)) return;
-        char *lb = smem + (s % kNS) * kStage;
+        char *lb = smem + (s & 1) * kStage;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if ((int64_t)s * 32 + a_ck[k] * 8 >= K)
-            *reinterpret_cast<u32x4 *>(lb + (4 * wave + k) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-          if ((int64_t)s * 32 + b_ck[k] * 8 >= K)
-            *reinterpret_cast<u32x4 *>(lb + kOpStage + (4 * wave + k) * 1024 + lane * 16) =
+        for (int k = 0; k < 8; ++k)
+          if ((int64_t)s * kBKv + load_chunk(k) * 8 >= K) {
+            *reinterpret_cast<u32x4 *>(lb + (8 * wave + k) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(lb + kOpStage + (8 * wave + k) * 1024 + lane * 16) =
                 u32x4{0u, 0u, 0u, 0u};
-        }
+          }
       };
-      // s_waitcnt immediates (gfx9): vmcnt in [3:0] and [15:14], expcnt [6:4] = 7 and
-      // lgkmcnt [11:8] = 15 (no wait on those)
-      constexpr int kVm16 = 0x0f70 | (16 & 15) | ((16 >> 4) << 14);  // <= 16 loads in flight
-      constexpr int kVm12 = 0x0f70 | (12 & 15) | ((12 >> 4) << 14);  // <= 12 loads in flight
-      constexpr int kLgkm0 = 0xc07f;                                 // lgkmcnt(0) only
-      static_assert(kNS == 4, "the vmcnt targets assume a 4-stage ring of 8 loads per stage");
+      constexpr int kVm0 = 0x0f70;    // s_waitcnt vmcnt(0) only (gfx9 encoding)
+      constexpr int kLgkm0 = 0xc07f;  // s_waitcnt lgkmcnt(0) only
 
       auto read_frag = [&](const char *op, int wbase, int i, int q) -> u32x4 {
         const int R = wbase + 32 * i + (lane & 31);
-        return *reinterpret_cast<const u32x4 *>(op + R * 64 + (((2 * q + g) ^ swz_lane) << 4));
+        return *reinterpret_cast<const u32x4 *>(op + R * 128 + (((2 * q + g) ^ swz_lane) << 4));
       };
-      // fragment reads of K slice q (16 elements) of stage s, in the order the MFMAs
-      // consume them: A0, B0..B3, A1..A3
-      auto read_frags = [&](int s, int q, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
-        const char *lb = smem + (s % kNS) * kStage;
-        fa[0] = read_frag(lb, wm * 128, 0, q);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = read_frag(lb + kOpStage, wn * 128, j, q);
-#pragma unroll
-        for (int i = 1; i < 4; ++i) fa[i] = read_frag(lb, wm * 128, i, q);
+      // Fragment read p (0..7) of K slice q (0..3, 16 elements each) of stage s, in the
+      // order the MFMAs consume them: A0, B0..B3, A1..A3.
+      auto read_one = [&](int s, int q, int p, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+        const char *lb = smem + (s & 1) * kStage;
+        if (p == 0)
+          fa[0] = read_frag(lb, wm * 128, 0, q);
+        else if (p < 5)
+          fb[p - 1] = read_frag(lb + kOpStage, wn * 128, p - 1, q);
+        else
+          fa[p - 4] = read_frag(lb, wm * 128, p - 4, q);
       };
-      // 16 MFMAs of one K slice, with the next slice's 8 LDS reads and (optionally) 4
-      // global->LDS loads spread between them
-      auto mma_slice = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], bool interleave, bool vmem) {
+      // One K slice: 16 MFMAs on fragments (ca, cb) in the order (i, j) = (p/4, p%4),
+      // with fragment read p of slice rq of stage rs (into na, nb) beside MFMA p for
+      // p < 8, so the next slice's operands land well before it starts, and, if
+      // ls >= 0, all 16 loads of stage ls (A then B) one per MFMA.  A scheduling fence
+      // after every step keeps exactly this order.
+      auto slice = [&](const u32x4 (&ca)[4], const u32x4 (&cb)[4], u32x4 (&na)[4], u32x4 (&nb)[4],
+                       bool rd, int rs, int rq, int ls) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
-        if (interleave) {
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // one LDS read
-            if (vmem && x < 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // two MFMAs
-          }
+        for (int p = 0; p < 16; ++p) {
+          if (rd && p < 8) read_one(rs, rq, p, na, nb);
+          if (ls >= 0) issue_one(ls, p >> 3, p & 7);
+          Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      };
+      // The last slice of stage kt: 8 MFMAs; then, if there is a next stage, wait for
+      // its loads, publish it (barrier) and read its first slice beside the other 8.
+      auto slice_last = [&](const u32x4 (&ca)[4], const u32x4 (&cb)[4], u32x4 (&na)[4], u32x4 (&nb)[4],
+                            bool next, int ns) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (next) {
+          __builtin_amdgcn_s_waitcnt(kVm0);  // this wave's loads of stage ns have landed
+          fix_tail(ns);
+          __builtin_amdgcn_s_waitcnt(kLgkm0);  // and its reads of this stage are done
+          __builtin_amdgcn_s_barrier();
+        }
+#pragma unroll
+        for (int p = 8; p < 16; ++p) {
+          if (next) read_one(ns, 0, p - 8, na, nb);
+          Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       };
 
-      // ---- prologue: stages 0 .. kNS-2 in flight, stage 0 visible ----
+      // ---- prologue: stage 0 loaded and visible, its first slice read ----
 #pragma unroll
-      for (int s = 0; s < kNS - 1; ++s) {
-        issue_a(s);
-        issue_b(s);
-      }
-      __builtin_amdgcn_s_waitcnt(kVm16);  // this wave's stage-0 loads have landed
+      for (int k8 = 0; k8 < 16; ++k8) issue_one(0, k8 >> 3, k8 & 7);
+      __builtin_amdgcn_s_waitcnt(kVm0);
       fix_tail(0);
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
       u32x4 F0a[4], F0b[4], F1a[4], F1b[4];
-      read_frags(0, 0, F0a, F0b);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) read_one(0, 0, p, F0a, F0b);
       __builtin_amdgcn_sched_barrier(0);
 
-      // Stages 0 .. nkv-2: each iteration also brings stage kt+1 into view and issues
-      // stage kt+3 (A before the barrier, B after it, each spread over 16 MFMAs).  The
-      // last stage is peeled so the loop body is one straight path.
+      // Stage kt: stage kt+1 streams into the other buffer (which held stage kt-1,
+      // released by the previous barrier) during the first slice; the last slice
+      // publishes it.  The last stage is peeled so the loop body is one straight path.
       for (int kt = 0; kt + 1 < nkv; ++kt) {
-        issue_a(kt + kNS - 1);  // into the buffer stage kt-1 used
-        read_frags(kt, 1, F1a, F1b);
-        mma_slice(F0a, F0b, true, true);
-        // in flight after stage kt+1's loads: A, B of stage kt+2 and A of stage kt+3
-        __builtin_amdgcn_s_waitcnt(kVm12);
-        fix_tail(kt + 1);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's reads of stage kt are done
-        __builtin_amdgcn_s_barrier();
-        issue_b(kt + kNS - 1);
-        read_frags(kt + 1, 0, F0a, F0b);
-        mma_slice(F1a, F1b, true, true);
+        slice(F0a, F0b, F1a, F1b, true, kt, 1, kt + 1);
+        slice(F1a, F1b, F0a, F0b, true, kt, 2, -1);
+        slice(F0a, F0b, F1a, F1b, true, kt, 3, -1);
+        slice_last(F1a, F1b, F0a, F0b, true, kt + 1);
       }
-      read_frags(nkv - 1, 1, F1a, F1b);
-      mma_slice(F0a, F0b, true, false);
-      mma_slice(F1a, F1b, false, false);
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // drain the trailing loads (they target free buffers)
+      slice(F0a, F0b, F1a, F1b, true, nkv - 1, 1, -1);
+      slice(F1a, F1b, F0a, F0b, true, nkv - 1, 2, -1);
+      slice(F0a, F0b, F1a, F1b, true, nkv - 1, 3, -1);
+      slice_last(F1a, F1b, F0a, F0b, false, 0);
       __syncthreads();  // every wave is done with the ring before epilogues reuse LDS
     }
 
@@ -551,8 +563,47 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // acc[i][j][r] holds tile row  wm*128 + i*32 + 8*(r/4) + 4*g + (r%4)
     //               and tile col  wn*128 + j*32 + (lane % 32).
     // Indices below are tile-local 32-bit; tile origins are uniform.
-    const int row0 = wm * 128 + (g << 2);     // + i*32 + 8*(r/4) + (r%4)
-    const int col0 = wn * 128 + (lane & 31);  // + j*32
+    // Epilogue addresses depend only on the lane; computed from an opaque copy of the
+    // lane index here, they cannot be hoisted out of the tile loop and held in
+    // registers through the main loop.
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int row0 = wm * 128 + ((elane >> 5) << 2);  // + i*32 + 8*(r/4) + (r%4)
+    const int col0 = wn * 128 + (elane & 31);         // + j*32
+    // bf16 epilogues stage a 256 x 256 bf16 tile in LDS column-major, Ls[col][row] with
+    // kLsPitch-byte lines (a lane's 4 consecutive rows are one 8-byte write), and write
+    // it out row by row with transposing LDS reads: in a group of 16 lanes, lane i
+    // names 4 consecutive rows (mb + 4 (i % 4)) of column line cb + i / 4 and receives
+    // row mb + i over columns cb .. cb + 3; two reads give 8 columns, one 16-byte store.
+    // A wave store writes 64 contiguous bytes of each of 16 rows.  Row m (< m_valid)
+    // goes to dst + m * ld elements; colmap(cb) gives the destination column of tile
+    // columns cb .. cb + 7, or -1 to skip them.
+    auto ls_put4 = [&](int col, int c0, float d0, float d1, float d2, float d3) {
+      u32x2 v;
+      v.x = bf16_rne(d0) | (bf16_rne(d1) << 16);
+      v.y = bf16_rne(d2) | (bf16_rne(d3) << 16);
+      *reinterpret_cast<u32x2 *>(smem + col * kLsPitch + c0 * 2) = v;
+    };
+    auto ls_store_rows = [&](char *dst, int64_t ld, int m_valid, auto &&colmap) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const int li = elane & 15, g4 = elane >> 4;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        const int mb = wave * 64 + vb * 16;
+#pragma unroll 2
+        for (int k = 0; k < 8; ++k) {
+          const int cb = k * 32 + g4 * 8;  // first of this lane's 8 columns
+          const char *src = smem + (cb + (li >> 2)) * kLsPitch + (mb + 4 * (li & 3)) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(src));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4 __attribute__((address_space(3))) *)(src + 4 * kLsPitch));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const int64_t c = colmap(k, cb);
+          if (c >= 0 && mb + li < m_valid)
+            *reinterpret_cast<u32x4 *>(dst + ((int64_t)(mb + li) * ld + c) * 2) = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+      }
+    };
     if constexpr (KIND == kFwd) {
       const int64_t v_tile = mi * kTile;
       const int n_rows = (int)imin(a.V - v_tile, kTile);  // valid vocabulary rows
@@ -601,10 +652,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         st_s[j] = s;
         st_u[j] = u;
         st_zy[j] = zy;
-        if (wm == 1 && lane < 32) xch[col] = make_float4(mx, s, u, zy);
+        if (wm == 1 && elane < 32) xch[col] = make_float4(mx, s, u, zy);
       }
       __syncthreads();
-      if (wm == 0 && lane < 32) {
+      if (wm == 0 && elane < 32) {
         float4 *out = reinterpret_cast<float4 *>(a.part) + mi * a.T + t_tile;
         const int n_cols = (int)imin(a.T - t_tile, kTile);
 #pragma unroll
@@ -620,7 +671,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     } else if constexpr (KIND == kDlogits) {
       const int64_t v_tile = mi * kTile;  // split-local first column
       const int n_live = (int)imin(a.Ws - v_tile, kTile);
-      const int n_cols = (int)imin(a.ld_d - v_tile, kTile);
+      const int n_cols = (int)imin(cdiv(a.Ws, kPer) * kPer - v_tile, kTile);  // written columns
+      const int64_t t_pad = cdiv(a.T, kPer) * kPer;  // tokens written, zero padding included
       // the pair's two token tiles (the second may be missing)
       const int64_t pt0 = uni(a.tile_list[2 * ni]);
       const int64_t pt1 = (2 * ni + 1 < a.n_skip_tiles) ? uni(a.tile_list[2 * ni + 1]) : -1;
@@ -664,13 +716,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
               d[c] = (c0 + c < lim) ? val : 0.f;
             }
             if constexpr (kV2) {
-              u32x2 v;
-              v.x = bf16_rne(d[0]) | (bf16_rne(d[1]) << 16);
-              v.y = bf16_rne(d[2]) | (bf16_rne(d[3]) << 16);
-              *reinterpret_cast<u32x2 *>(Ls + col * kLsPitch + c0 * 2) = v;
+              ls_put4(col, c0, d[0], d[1], d[2], d[3]);
             } else {
               if (tok && c0 < n_cols) store4(Dd + t * a.ld_d + c0, d[0], d[1], d[2], d[3]);
-              if (tile >= 0 && t < a.ld_t) {  // a token or its zero padding
+              if (tile >= 0 && t < t_pad) {  // a token or its zero padding
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                   if (c0 + c < n_live) store1(Dv + (int64_t)(c0 + c) * a.ld_t + t, d[c]);
@@ -686,40 +735,21 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         // 512-byte rows per store
 #pragma unroll 4
         for (int k = 0; k < 32; ++k) {
-          const int tl = wave * 64 + 2 * k + (lane >> 5);  // token within the pair tile
-          const int cc = (lane & 31) * 8;                  // first column of the chunk
+          const int tl = wave * 64 + 2 * k + (elane >> 5);  // token within the pair tile
+          const int cc = (elane & 31) * 8;                  // first column of the chunk
           const u32x4 v = *reinterpret_cast<const u32x4 *>(Ls + tl * kLsPitch + cc * 2);
           const int64_t tile = (tl >> 7) ? pt1 : pt0;
           const int64_t t = tile * kSkipTile + (tl & 127);
           if (tile >= 0 && t < a.T && cc < n_cols)
             *reinterpret_cast<u32x4 *>(Db + (t * a.ld_d + cc) * 2) = v;
         }
-        // vocabulary-major: transposing LDS reads.  In a group of 16 lanes, lane i
-        // names 4 consecutive vocabulary entries (mb + 4 (i % 4)) of token row
-        // tb + i / 4 and receives vocabulary row mb + i over tokens tb .. tb + 3; two
-        // reads give 8 tokens, one 16-byte store.  A wave store writes 64 contiguous
-        // bytes of each of 16 vocabulary rows.
-        const int li = lane & 15, g4 = lane >> 4;
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb) {
-          const int mb = wave * 64 + vb * 16;
-#pragma unroll 2
-          for (int k = 0; k < 8; ++k) {
-            const int tb = k * 32 + g4 * 8;  // first of this lane's 8 tokens
-            const char *src = Ls + (tb + (li >> 2)) * kLsPitch + (mb + 4 * (li & 3)) * 2;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)(src));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)(src + 4 * kLsPitch));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            const int64_t tile = (k >> 2) ? pt1 : pt0;  // tb / 128
-            const int64_t t = tile * kSkipTile + (tb & 127);
-            if (tile >= 0 && t < a.ld_t && mb + li < n_live)
-              *reinterpret_cast<u32x4 *>(Dvb + ((int64_t)(mb + li) * a.ld_t + t) * 2) =
-                  u32x4{l2.x, l2.y, h2.x, h2.y};
-          }
-        }
+        // vocabulary-major: rows v of the split, tokens of the pair (zero padding to a
+        // whole 16-byte chunk included)
+        ls_store_rows(Dvb, a.ld_t, n_live, [&](int k, int cb) -> int64_t {
+          const int64_t tile = (k >> 2) ? pt1 : pt0;  // cb / 128
+          const int64_t t = tile * kSkipTile + (cb & 127);
+          return (tile >= 0 && t < t_pad) ? t : -1;
+        });
       }
     } else if constexpr (KIND == kDhidden) {
       const int n_rows = (int)(span_s1 - span_s0);
@@ -727,39 +757,105 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int n_cols = (int)imin(a.H - n_tile, kTile);
       float *base = a.dh_acc + span_s0 * a.H + n_tile;
       const uint32_t ldh = (uint32_t)a.H;
+      if constexpr (kV2) {
+        // fp32 sum over splits through LDS, half a tile at a time: in phase p every wave
+        // writes its row blocks i = 2p, 2p+1 as they sit in registers,
+        // [wave][i - 2p][j][r][lane] (constant offsets from one per-lane base); then wave
+        // w takes the 32 rows of block (wm, i) = (w / 2, 2p + w % 2) and adds the
+        // earlier splits' sum with 16-byte loads and stores (4 consecutive columns are
+        // 4 consecutive lanes of one register).
+        const int c4 = elane * 4;  // this lane's 4 columns in the row it handles
+        // column c4 sits in the registers of wave (wm, wn = c4 / 128), j = c4 / 32 % 4
+        const int lds_col = (c4 >> 7) * 32768 + ((c4 >> 5) & 3) * 4096 + (c4 & 31) * 4;
+        char *wb = smem + wave * 32768 + elane * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
-          if (row >= n_rows) continue;
-          float *prow = base + (uint32_t)row * ldh;
+          for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = col0 + j * 32;
-            if (col < n_cols) prow[col] = acc[i][j][r];
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                *reinterpret_cast<float *>(wb + ((ii * 4 + j) * 16 + r) * 256) = acc[2 * p + ii][j][r];
+          __syncthreads();
+          const int rwm = wave >> 1, rii = wave & 1;  // the row block this wave stores
+          const int row_b = rwm * 128 + (2 * p + rii) * 32;
+          const int src_b = lds_col + rwm * 65536 + rii * 16384;  // + (g, r) of the row
+#pragma unroll
+          for (int k0 = 0; k0 < 32; k0 += 8) {
+            float4 prev[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const int row = row_b + k0 + kk;
+              const bool ok = !a.first_split && row < n_rows && c4 < n_cols;
+              prev[kk] = ok ? *reinterpret_cast<const float4 *>(base + (uint32_t)row * ldh + c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const int rr = k0 + kk, row = row_b + rr;  // rr = 4 g + 8 (r / 4) + r % 4
+              const int src = src_b + (((rr >> 3) & 3) * 4 + (rr & 3)) * 256 + ((rr >> 2) & 1) * 128;
+              if (row < n_rows && c4 < n_cols) {
+                float4 v = *reinterpret_cast<const float4 *>(smem + src);
+                v.x += prev[kk].x;
+                v.y += prev[kk].y;
+                v.z += prev[kk].z;
+                v.w += prev[kk].w;
+                *reinterpret_cast<float4 *>(base + (uint32_t)row * ldh + c4) = v;
+              }
+            }
           }
+          __syncthreads();
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
+            if (row >= n_rows) continue;
+            float *prow = base + (uint32_t)row * ldh;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int col = col0 + j * 32;
+              if (col < n_cols) prow[col] = acc[i][j][r];
+            }
+          }
+      }
     } else {
       const int64_t v_tile = mi * kTile;
       const int n_rows = (int)imin(a.Ws - v_tile, kTile);
       const int64_t n_tile = ni * kTile;
       const int n_cols = (int)imin(a.H - n_tile, kTile);
       T *base = reinterpret_cast<T *>(a.dW) + (a.v_base + v_tile) * a.H + n_tile;
-      const uint32_t ldw = (uint32_t)a.H;
+      if constexpr (kV2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
-          if (row >= n_rows) continue;
-          T *prow = base + (uint32_t)row * ldw;
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = col0 + j * 32;
-            if (col < n_cols) store1(prow + col, acc[i][j][r]);
+            for (int q = 0; q < 4; ++q)
+              ls_put4(col0 + j * 32, row0 + i * 32 + q * 8, acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        __syncthreads();
+        ls_store_rows(reinterpret_cast<char *>(base), a.H, n_rows,
+                      [&](int, int cb) -> int64_t { return cb < n_cols ? cb : -1; });
+      } else {
+        const uint32_t ldw = (uint32_t)a.H;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
+            if (row >= n_rows) continue;
+            T *prow = base + (uint32_t)row * ldw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int col = col0 + j * 32;
+              if (col < n_cols) store1(prow + col, acc[i][j][r]);
+            }
           }
-        }
+      }
     }
     __syncthreads();  // LDS is reused by the next tile's prologue
   }

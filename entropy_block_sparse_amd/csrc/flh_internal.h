@@ -29,7 +29,8 @@ struct GemmArgs {
   // vocabulary split (d-logits, dH, dW)
   int64_t v_base;          // first vocabulary row of the split
   int32_t Ws;              // live width of the split
-  int32_t ld_d;            // row stride (elements) of the d-logits staging buffer
+  int32_t ld_d;            // row stride (elements) of the token-major d-logits staging;
+                           // columns [0, W_s rounded up to 16 bytes) are written
   // inputs
   const void *h;           // [T, H]
   const void *W;           // [V, H]
@@ -48,10 +49,11 @@ struct GemmArgs {
   float *part;             // forward partials [ceil(V/256)][T][4]
   void *D;                 // d-logits staging [T][ld_d]
   void *Dt;                // the same d-logits transposed: [W_s][ld_t]
-  const void *Wt;          // W transposed: [H][ld_wt]
+  const void *Wt;          // this split's rows of W, transposed: [H][ld_wt]
   const void *ht;          // h transposed: [H][ld_t]
-  int64_t ld_wt;           // row stride (elements) of Wt: V rounded up to 16 bytes
-  int64_t ld_t;            // row stride (elements) of ht and Dt: T rounded up to 16 bytes
+  int64_t ld_wt;           // row stride (elements) of Wt, >= W_s (zero padded)
+  int64_t ld_t;            // row stride (elements) of ht and Dt, >= T; tokens up to T
+                           // rounded up to 16 bytes are written (zeros past T)
   float *dh_acc;           // fp32 hidden-gradient accumulator [T][H]
   int32_t first_split;     // dH: 1 -> overwrite, 0 -> accumulate
   int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
@@ -74,10 +76,13 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
 hipError_t launch_combine(int64_t T, int64_t V, const float *part, const int64_t *targets,
                           float *logprob, float *entropy, float *lse, hipStream_t st);
 
-// out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for R <= r < ld_out.
-// in: [R][C] row-major; out: [C][ld_out]; elements of esz bytes (2 or 4).
+// Blocked transpose: rows of `in` ([R][C] row-major, elements of esz bytes, 2 or 4)
+// are taken in blocks of `block` rows (a multiple of 64; 0 = one block of R rows);
+// block b becomes its own [C][ld_out] matrix at out + b * C * ld_out:
+// out_b[c][r] = in[b * block + r][c] for rows of the block, and 0 for the rest of
+// [0, ld_out).
 hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
-                            hipStream_t st);
+                            int64_t block, hipStream_t st);
 
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc,
                            const uint8_t *mask, void *dh, hipStream_t st);

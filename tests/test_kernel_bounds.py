@@ -21,11 +21,17 @@ tid = np.arange(256)
 lane = tid & 63
 wave = tid >> 6
 U32 = (1 << 32)
-OPSTAGE = 256 * 64  # bytes of one operand in one stage of the bf16 LDS ring
+OPSTAGE = 256 * 128  # bytes of one operand in one stage of the bf16 LDS double buffer
 
 
 def cdiv(a, b):
     return (a + b - 1) // b
+
+
+def pad_ld(n):
+    """Workspace row stride: a multiple of 64 elements, odd in units of 64."""
+    ld = cdiv(n, 64) * 64
+    return ld + 64 if (ld // 64) % 2 == 0 else ld
 
 
 class Buf:
@@ -100,43 +106,50 @@ def rsrc_v2(src, K, what):
             assert 0 <= base and base + nb <= src.buf.n, \
                 f"{what}: descriptor [{base}, {base + nb}) outside {src.buf.name} ({src.buf.n})"
     # lane offset (row within the half, chunk) plus the stage offset fits 32 bits
-    assert 127 * src.ldb + 48 + cdiv(K, 32) * 64 < U32, f"{what}: 32-bit offset overflow"
+    assert 127 * src.ldb + 112 + cdiv(K, 64) * 128 < U32, f"{what}: 32-bit offset overflow"
 
 
-def transpose_model(inp, R, C, out, ld_out, esz, what):
-    """out[c][r] = in[r][c] over 64 x 64 tiles: 16-byte loads where the vector is whole,
+def transpose_model(inp, R, C, out, ld_out, esz, what, block=0):
+    """Blocked transpose over 64 x 64 tiles: block b of `block` rows of `in` becomes
+    out_b = out + b * C * ld_out, [C][ld_out].  16-byte loads where the vector is whole,
     element loads otherwise; stores likewise.  Checks bounds and that every output
-    element (c < C, r < ld_out) is written exactly once."""
+    element (block, c < C, r < ld_out) is written exactly once."""
     kV = 16 // esz
-    written = np.zeros((C, ld_out), np.int32)
-    for t0 in range(cdiv(ld_out, 64)):
-        for c0t in range(cdiv(C, 64)):
-            r0, c0 = t0 * 64, c0t * 64
-            idx = np.arange(64 * (64 // kV))
-            rr, cv = idx // (64 // kV), (idx % (64 // kV)) * kV
-            r, c = r0 + rr, c0 + cv
-            whole = (r < R) & (c + kV <= C)
-            inp.check((r[whole] * C + c[whole]) * esz, 16, what + " load")
-            for e in range(kV):
-                ok = ~whole & (r < R) & (c + e < C)
-                inp.check((r[ok] * C + c[ok] + e) * esz, esz, what + " load1")
-            cc, rv = idx // (64 // kV), (idx % (64 // kV)) * kV
-            c, r = c0 + cc, r0 + rv
-            live = (c < C) & (r < ld_out)
-            whole = live & (r + kV <= ld_out)
-            out.check((c[whole] * ld_out + r[whole]) * esz, 16, what + " store")
-            for e in range(kV):
-                written[c[whole], r[whole] + e] += 1
-                ok = live & ~whole & (r + e < ld_out)
-                out.check((c[ok] * ld_out + r[ok] + e) * esz, esz, what + " store1")
-                written[c[ok], r[ok] + e] += 1
+    block = block or R
+    n_blocks = cdiv(R, block)
+    written = np.zeros((n_blocks, C, ld_out), np.int32)
+    for blk in range(n_blocks):
+        R_blk = min(block, R - blk * block)
+        for t0 in range(cdiv(ld_out, 64)):
+            for c0t in range(cdiv(C, 64)):
+                rb, c0 = t0 * 64, c0t * 64
+                idx = np.arange(64 * (64 // kV))
+                rr, cv = idx // (64 // kV), (idx % (64 // kV)) * kV
+                r, c = blk * block + rb + rr, c0 + cv
+                live = rb + rr < R_blk
+                whole = live & (c + kV <= C)
+                inp.check((r[whole] * C + c[whole]) * esz, 16, what + " load")
+                for e in range(kV):
+                    ok = ~whole & live & (c + e < C)
+                    inp.check((r[ok] * C + c[ok] + e) * esz, esz, what + " load1")
+                cc, rv = idx // (64 // kV), (idx % (64 // kV)) * kV
+                c, r = c0 + cc, rb + rv
+                live = (c < C) & (r < ld_out)
+                whole = live & (r + kV <= ld_out)
+                base = blk * C * ld_out
+                out.check((base + c[whole] * ld_out + r[whole]) * esz, 16, what + " store")
+                for e in range(kV):
+                    written[blk, c[whole], r[whole] + e] += 1
+                    ok = live & ~whole & (r + e < ld_out)
+                    out.check((base + c[ok] * ld_out + r[ok] + e) * esz, esz, what + " store1")
+                    written[blk, c[ok], r[ok] + e] += 1
     assert (written == 1).all(), f"{what}: output not covered exactly once"
 
 
 LS_PITCH, LDS_DLG = 528, 256 * 528  # bf16 d-logits epilogue: LDS tile pitch and size
 
 
-def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, v0, n_live, n_cols):
+def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols):
     """bf16 d-logits epilogue: the tile is staged token-major in LDS, then written
     token-major (16-byte chunks of 512-byte rows) and vocabulary-major (transposing
     LDS reads, 16-byte stores)."""
@@ -162,7 +175,7 @@ def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, v0, n_live, n_cols):
         assert (a % 8 == 0).all() and (a + 4 * LS_PITCH + 8 <= LDS_DLG).all()
         tile = pair[1] if k >> 2 else pair[0]
         t = tile * SKIP + (tb & 127)
-        ok = (tile >= 0) & (t < ld_t) & (mb + li < n_live)
+        ok = (tile >= 0) & (t < t_pad) & (mb + li < n_live)
         Dt.check(((v0 + mb[ok] + li[ok]) * ld_t + t[ok]) * 2, 16, "dlg store^T (LDS)")
 
 
@@ -174,11 +187,12 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     h = Buf("h", T * H * esz)
     W = Buf("W", V * H * esz)
     w_max = min(V, S_split)
-    ld_max = cdiv(w_max, kper) * kper
-    ld_wt, ld_t = cdiv(V, kper) * kper, cdiv(T, kper) * kper
+    ld_max = pad_ld(w_max)
+    ld_wt, ld_t = pad_ld(w_max), pad_ld(T)
+    t_pad = cdiv(T, kper) * kper  # tokens of the vocabulary-major staging that are written
     D = Buf("D", T * ld_max * esz)
     Dt = Buf("Dt", w_max * ld_t * esz)
-    Wt = Buf("Wt", H * ld_wt * esz)
+    Wt = Buf("Wt", cdiv(V, S_split) * H * ld_wt * esz)
     ht = Buf("ht", H * ld_t * esz)
     part = Buf("part", cdiv(V, TILE) * T * 16)
     acc = Buf("acc", T * H * 4)
@@ -204,7 +218,7 @@ def model(T, H, V, S_split, esz, mask, sample=False):
 
     # ---- backward: transposed copies, work lists ----
     if not sample:
-        transpose_model(W, V, H, Wt, ld_wt, esz, "W^T")
+        transpose_model(W, V, H, Wt, ld_wt, esz, "W^T", block=S_split)
         transpose_model(h, T, H, ht, ld_t, esz, "h^T")
     flags = S.tile_flags(mask, SKIP)
     n_skip = len(flags)
@@ -215,15 +229,16 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     for sp in _pick(cdiv(V, S_split), sample):
         Ws = min(S_split, V - sp * S_split)
         v_base = sp * S_split
-        ld_d = cdiv(Ws, kper) * kper
-        assert ld_d <= ld_max and v_base + ld_d <= ld_wt
+        ld_d = pad_ld(Ws)
+        w_pad = cdiv(Ws, kper) * kper  # columns of the token-major staging that are written
+        assert ld_d <= ld_max and w_pad <= ld_wt and w_pad <= ld_d and t_pad <= ld_t
         # ---- d-logits ----
-        m_tiles = cdiv(ld_d, TILE)
+        m_tiles = cdiv(Ws, TILE)
         n_pairs_gemm, n_pairs_all = cdiv(n_act, 2), cdiv(n_skip, 2)
         for mi in _pick(m_tiles, sample):
             v0 = mi * TILE
             assert v0 <= Ws - 1
-            n_live, n_cols = min(Ws - v0, TILE), min(ld_d - v0, TILE)
+            n_live, n_cols = min(Ws - v0, TILE), min(w_pad - v0, TILE)
             wb = (v_base + v0) * ldb
             for ni in _pick(n_pairs_gemm, sample):
                 loads(Src(W, wb, min(Ws - v0, 128), wb + 128 * ldb, Ws - v0 - 128, ldb), H, "dlg A")
@@ -233,13 +248,13 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                           min(T - t1 * SKIP, 128) if t1 >= 0 else 0, ldb), H, "dlg B")
                 pair = (t0, t1)
                 if v2:
-                    dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, v0, n_live, n_cols)
+                    dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols)
                     continue
                 for j in range(4):
                     col = col_q + j * 32
                     tl = np.array([pair[x] for x in col >> 7])
                     t = tl * SKIP + (col & 127)
-                    tok, tokp = (tl >= 0) & (t < T), (tl >= 0) & (t < ld_t)
+                    tok, tokp = (tl >= 0) & (t < T), (tl >= 0) & (t < t_pad)
                     for i, q in itertools.product(range(4), range(4)):
                         c0 = row_q + i * 32 + q * 8
                         ok = tok & (c0 < n_cols)
@@ -248,7 +263,7 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                             ok = tokp & (c0 + c < n_live)
                             Dt.check(((v0 + c0[ok] + c) * ld_t + t[ok]) * esz, esz, "dlg store^T")
             for p in [x + n_pairs_gemm for x in _pick(n_pairs_all - n_pairs_gemm, sample)]:
-                c1 = min(v0 + TILE, ld_d)
+                c1 = min(v0 + TILE, w_pad)
                 chunks = TILE // kper
                 idx = np.arange(TILE * chunks)
                 row, ch = idx // chunks, idx % chunks
@@ -266,7 +281,7 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                 v = v0 + vr
                 tl = np.array([tile_list[x] if x < n_skip else -1 for x in e])
                 t = tl * SKIP + vec * kper
-                ok = (tl >= 0) & (v < min(v0 + TILE, Ws)) & (t < ld_t)
+                ok = (tl >= 0) & (v < min(v0 + TILE, Ws)) & (t < t_pad)
                 Dt.check((v[ok] * ld_t + t[ok]) * esz, 16, "dlg zero^T")
         # ---- dHidden over span tiles: A = staging rows, B = W^T rows from v_base ----
         ldd, ldw = ld_d * esz, ld_wt * esz
@@ -274,9 +289,16 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                                               _pick(cdiv(H, TILE), sample)):
             nr, n0 = s1 - s0, ni * TILE
             loads(Src(D, s0 * ldd, min(nr, 128), (s0 + 128) * ldd, nr - 128, ldd), Ws, "dh A")
-            wt = n0 * ldw + v_base * esz
-            loads(Src(Wt, wt, min(H - n0, 128), wt + 128 * ldw, H - n0 - 128, ldw, v_base * esz), Ws,
-                  "dh B")
+            wt = (sp * H + n0) * ldw
+            loads(Src(Wt, wt, min(H - n0, 128), wt + 128 * ldw, H - n0 - 128, ldw), Ws, "dh B")
+            if v2:
+                # read-modify-write of whole rows, 16 bytes per lane (4 columns)
+                c4 = lane * 4
+                for p, rr in itertools.product(range(2), range(32)):
+                    row = (wave >> 1) * 128 + (2 * p + (wave & 1)) * 32 + rr
+                    ok = (row < s1 - s0) & (c4 < min(H - n0, TILE))
+                    acc.check(((s0 + row[ok]) * H + n0 + c4[ok]) * 4, 16, "dh rmw")
+                continue
             for i, r in itertools.product(range(4), range(16)):
                 t = s0 + row_q + i * 32 + ((r >> 2) << 3) + (r & 3)
                 for j in range(4):
@@ -289,6 +311,15 @@ def model(T, H, V, S_split, esz, mask, sample=False):
             v0, n0 = mi * TILE, ni * TILE
             loads(Src(Dt, v0 * ldt, min(Ws - v0, 128), (v0 + 128) * ldt, Ws - v0 - 128, ldt), T, "dw A")
             loads(Src(ht, n0 * ldt, min(H - n0, 128), (n0 + 128) * ldt, H - n0 - 128, ldt), T, "dw B")
+            if v2:
+                # LDS-staged rows, 16-byte stores (8 columns) via transposing reads
+                li, g4 = lane & 15, lane >> 4
+                for vb, k in itertools.product(range(4), range(8)):
+                    m = wave * 64 + vb * 16 + li
+                    cb = k * 32 + g4 * 8
+                    ok = (m < min(Ws - v0, TILE)) & (cb < min(H - n0, TILE))
+                    dW.check(((v_base + v0 + m[ok]) * H + n0 + cb[ok]) * esz, 16, "dw store (LDS)")
+                continue
             for i, r in itertools.product(range(4), range(16)):
                 v = v0 + row_q + i * 32 + ((r >> 2) << 3) + (r & 3)
                 for j in range(4):
@@ -297,13 +328,24 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                     dW.check(((v_base + v[ok]) * H + n[ok]) * esz, esz, "dw store")
 
     if v2:
-        # LDS: direct-load destinations and fragment reads stay inside one stage operand
-        for w, k, l in itertools.product(range(4), range(4), range(64)):
-            assert (4 * w + k) * 1024 + l * 16 + 16 <= OPSTAGE
-        for l in range(64):
-            for q, i, wb in itertools.product(range(2), range(4), (0, 128)):
+        # LDS: direct-load destinations (8 lanes per 128-byte row) and fragment reads
+        # stay inside one stage operand; the 16 rows a quarter-wave reads together
+        # cover all 64 banks
+        for w, k, l in itertools.product(range(4), range(8), range(64)):
+            row = 64 * w + 8 * k + (l >> 3)
+            phys = l & 7
+            assert (8 * w + k) * 1024 + l * 16 == row * 128 + phys * 16
+            assert (8 * w + k) * 1024 + l * 16 + 16 <= OPSTAGE
+        for q, i, wb in itertools.product(range(4), range(4), (0, 128)):
+            addrs = []
+            for l in range(64):
                 R = wb + 32 * i + (l & 31)
-                assert R * 64 + 64 <= OPSTAGE
+                a = R * 128 + ((((2 * q + (l >> 5)) ^ ((R >> 1) & 7))) << 4)
+                assert a + 16 <= OPSTAGE
+                addrs.append(a)
+            for quarter in range(4):
+                banks = {((addrs[x] // 4) + b) % 64 for x in range(16 * quarter, 16 * quarter + 16) for b in range(4)}
+                assert len(banks) == 64
 
 
 SHAPES = [
@@ -342,3 +384,61 @@ def test_bf16_descriptors_in_bounds(T, H, V, S_split):
     rng = np.random.default_rng(T + 3 * V)
     for mask in (np.ones(T, np.uint8), (rng.random(T) < 0.4).astype(np.uint8), np.zeros(T, np.uint8)):
         model(T, H, V, S_split, 2, mask)
+
+
+# ---- tile schedule: XCD-aware remap and grouped rasterization ---------------------------
+
+def _group_map(L, m_tiles, n_tiles, GM):
+    per_group = GM * n_tiles
+    g = L // per_group
+    r = L - g * per_group
+    first = g * GM
+    gm = min(m_tiles - first, GM)
+    return first + r % gm, r // gm
+
+
+def _tile_of(item, n_gemm, G, m_tiles, n_tiles, GM=8):
+    L = item
+    if G % 8 == 0:
+        r, b = divmod(item, G)
+        n_round = min(G, n_gemm - r * G)
+        x, q, rem8 = b & 7, n_round >> 3, n_round & 7
+        L = r * G + x * q + min(x, rem8) + (b >> 3)
+    return _group_map(L, m_tiles, n_tiles, GM)
+
+
+@pytest.mark.parametrize("m_tiles,n_tiles", [(1, 1), (31, 16), (64, 16), (501, 64), (7, 3), (64, 39), (3, 100)])
+@pytest.mark.parametrize("G", [256, 248, 64, 8, 1])
+def test_tile_schedule_is_a_bijection(m_tiles, n_tiles, G):
+    """Every workgroup tile of a launch is computed exactly once, whatever the grid."""
+    n_gemm = m_tiles * n_tiles
+    seen = [_tile_of(item, n_gemm, G, m_tiles, n_tiles) for item in range(n_gemm)]
+    assert sorted(seen) == [(mi, ni) for mi in range(m_tiles) for ni in range(n_tiles)]
+    # with the remap, the tiles one XCD holds in a round are a contiguous run of ids
+    if G % 8 == 0 and n_gemm > 8:
+        r0 = min(G, n_gemm)
+        for x in range(8):
+            ids = sorted(_l for _l in [(
+                (b & 7) * (r0 >> 3) + min(b & 7, r0 & 7) + (b >> 3)) for b in range(r0) if b & 7 == x])
+            assert ids == list(range(ids[0], ids[0] + len(ids))) if ids else True
+
+
+def test_dhidden_staging_map():
+    """bf16 hidden-gradient epilogue: the LDS offsets each wave writes its accumulators
+    to and the offsets the storing waves read back name the same (row, column)."""
+    written = {}
+    for w, l, p, ii, j, r in itertools.product(range(4), range(64), range(2), range(2), range(4), range(16)):
+        wm, wn, i = w >> 1, w & 1, 2 * p + ii
+        row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)
+        col = wn * 128 + j * 32 + (l & 31)
+        off = w * 32768 + ((ii * 4 + j) * 16 + r) * 256 + l * 4
+        assert 0 <= off and off + 4 <= 131072 and (p, off) not in written
+        written[(p, off)] = (row, col)
+    for p, w, l, rr in itertools.product(range(2), range(4), range(64), range(32)):
+        c4 = l * 4
+        lds_col = (c4 >> 7) * 32768 + ((c4 >> 5) & 3) * 4096 + (c4 & 31) * 4
+        rwm, rii = w >> 1, w & 1
+        src = lds_col + rwm * 65536 + rii * 16384 + (((rr >> 3) & 3) * 4 + (rr & 3)) * 256 + ((rr >> 2) & 1) * 128
+        assert src % 16 == 0
+        for e in range(4):
+            assert written[(p, src + 4 * e)] == (rwm * 128 + (2 * p + rii) * 32 + rr, c4 + e)
