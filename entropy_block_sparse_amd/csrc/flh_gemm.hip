@@ -52,7 +52,8 @@ constexpr int kLdsBytes = 4 * kOpBytes;      // A and B, two stages (147456 B)
 // bf16 path: two stages of 64 K elements (128 bytes per row) per operand
 constexpr int kOpStage = kTile * 128;     // one operand, one stage: 32 KiB
 constexpr int kStage = 2 * kOpStage;      // 64 KiB
-constexpr int kLdsBytesV2 = 2 * kStage;   // 128 KiB
+constexpr int kLdsBytesV2 = 2 * kStage + 1024;  // 128 KiB + the prefetch scratch
+constexpr int kPfLds = 2 * kStage;                // prefetch scratch: 256 bytes per wave
 // bf16 d-logits epilogue: the 256 x 256 tile staged token-major in LDS, rows padded to
 // 528 bytes (16-byte aligned, consecutive rows 4 banks apart)
 constexpr int kLsPitch = 528;
@@ -459,6 +460,34 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         char *lb = smem + (s & 1) * kStage + op * kOpStage + (8 * wave + k) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, lb, 16, op ? b_vo[k] : a_vo[k], s * 128, 0, 0);
       };
+      // L2 prefetch.  The 32 workgroups of an XCD hold an 8 x 4 block of tiles and share
+      // operand rows through its L2; a line a stage needs that no sharer has fetched yet
+      // misses, and every sharer then waits for that miss.  So each workgroup touches,
+      // kPfAhead stages early, its share of the block's lines: half of a quarter of its
+      // A tile's rows per wave 0/1 (by its position along N) and an eighth of its B
+      // tile's rows in waves 2/3 (by its position along M), one 128-byte line per row
+      // per stage (two lanes, one per 64-byte half), with 4-byte loads into a scratch
+      // corner of LDS.  The load
+      // goes out after the stage's real loads, so the wait for those can leave it in
+      // flight (vector loads complete in order).
+      constexpr int kPfAhead = 3;
+      __amdgpu_buffer_rsrc_t rpf;
+      uint32_t pf_vo;
+      {
+        const bool isA = wave < 2;
+        const RowSrc &src = isA ? srcA : srcB;
+        const int row_u = isA ? 64 * (int)(ni & 3) + 32 * (wave & 1) : 32 * (int)(mi & 7);  // wave-uniform
+        const bool h1 = row_u >= 128;
+        const int64_t n = h1 ? src.n1 : src.n0;
+        rpf = rsrc(uni(h1 ? src.base1 : src.base0), uni(n > 0 ? n * src.ldb - src.trim : 0));
+        // lanes 0..31 touch the first 64 bytes of their row's line, lanes 32..63 the rest
+        pf_vo = (uint32_t)((int64_t)((row_u & 127) + (lane & 31)) * src.ldb) + (uint32_t)((lane >> 5) * 64);
+      }
+      const __amdgpu_buffer_rsrc_t rnull = rsrc(Wp, 0);
+      auto issue_pf = [&](int s) {  // always issued, so the vmcnt targets are constant
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s < nkv ? rpf : rnull, smem + kPfLds + wave * 256, 4, pf_vo,
+                                                 s * 128, 0, 0);
+      };
       // Last, partial K stage: chunks wholly past K were read from the next row (or
       // as zeros); overwrite them with zeros once this wave's loads of the stage have
       // landed.  A chunk that straddles K is kept: past K it holds the zero padding
@@ -476,6 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           }
       };
       constexpr int kVm0 = 0x0f70;    // s_waitcnt vmcnt(0) only (gfx9 encoding)
+      constexpr int kVm1 = 0x0f71;    // vmcnt(1): all but the latest (prefetch) load
       constexpr int kLgkm0 = 0xc07f;  // s_waitcnt lgkmcnt(0) only
 
       auto read_frag = [&](const char *op, int wbase, int i, int q) -> u32x4 {
@@ -499,11 +529,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // ls >= 0, all 16 loads of stage ls (A then B) one per MFMA.  A scheduling fence
       // after every step keeps exactly this order.
       auto slice = [&](const u32x4 (&ca)[4], const u32x4 (&cb)[4], u32x4 (&na)[4], u32x4 (&nb)[4],
-                       bool rd, int rs, int rq, int ls) {
+                       bool rd, int rs, int rq, int ls, int pfs = -1) {
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
           if (rd && p < 8) read_one(rs, rq, p, na, nb);
           if (ls >= 0) issue_one(ls, p >> 3, p & 7);
+          if (pfs >= 0 && p == 0) issue_pf(pfs);
           Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -518,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           __builtin_amdgcn_sched_barrier(0);
         }
         if (next) {
-          __builtin_amdgcn_s_waitcnt(kVm0);  // this wave's loads of stage ns have landed
+          __builtin_amdgcn_s_waitcnt(kVm1);  // this wave's loads of stage ns have landed
           fix_tail(ns);
           __builtin_amdgcn_s_waitcnt(kLgkm0);  // and its reads of this stage are done
           __builtin_amdgcn_s_barrier();
@@ -548,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // publishes it.  The last stage is peeled so the loop body is one straight path.
       for (int kt = 0; kt + 1 < nkv; ++kt) {
         slice(F0a, F0b, F1a, F1b, true, kt, 1, kt + 1);
-        slice(F1a, F1b, F0a, F0b, true, kt, 2, -1);
+        slice(F1a, F1b, F0a, F0b, true, kt, 2, -1, kt + kPfAhead);
         slice(F0a, F0b, F1a, F1b, true, kt, 3, -1);
         slice_last(F1a, F1b, F0a, F0b, true, kt + 1);
       }
@@ -556,6 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       slice(F1a, F1b, F0a, F0b, true, nkv - 1, 2, -1);
       slice(F0a, F0b, F1a, F1b, true, nkv - 1, 3, -1);
       slice_last(F1a, F1b, F0a, F0b, false, 0);
+      __builtin_amdgcn_s_waitcnt(kVm0);  // prefetches still in flight target LDS
       __syncthreads();  // every wave is done with the ring before epilogues reuse LDS
     }
 
