@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--active-frac", type=float, default=None, help="stress workload point")
     p.add_argument("--dense", action="store_true", help="dense fallback (no metadata)")
-    p.add_argument("--cpu-tokens", type=int, default=256, help="oracle slice (0 = skip)")
+    p.add_argument("--cpu-tokens", type=int, default=1024, help="oracle slice (0 = skip)")
     p.add_argument("--no-trace", action="store_true")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="run one device copy of this many MiB first (counter calibration)")

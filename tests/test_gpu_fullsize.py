@@ -1,0 +1,157 @@
+"""The HIP path at the full workload sizes, in the launch configuration bench.py times.
+
+At full size the fp64 oracle cannot afford every output, so:
+
+* spans, tile bitmap and active count: bit-exact against the oracle over all T;
+* forward outputs (logprob, entropy, lse) and d_hidden rows: on 256 sampled tokens
+  (first/last tokens, 128-token tile edges, span starts and ends, and random ones),
+  against the oracle's per-token definitions, which are exact at any T because each
+  token's outputs depend on its own hidden row alone (SkyRL #2376, "How it works");
+* every inactive d_hidden row: bitwise +0;
+* d_weight, which depends on every token, through identities that hold at any size:
+  each row of the d-logits sums to zero over the vocabulary (both the log-prob and the
+  entropy terms do), so sum_v dW[v, :] = 0; and <dH, h> = <dW, W> = sum D * z.
+
+The tolerances are the ones of the reduced-size parity tests: max abs 5e-3 for the
+forward outputs and relative Frobenius 1e-2 for the gradient rows.
+
+T-slices of configs 3-5 (1024 tokens chosen to straddle active and inactive runs) are
+also checked against the full oracle at full H and V.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from entropy_block_sparse_amd import flh_backward, flh_forward, flh_spans_build
+from oracle import lmhead as O
+from oracle import spans as S
+from tests.gpu_common import announce, cuda_device, host64
+from tests.helpers import max_abs, rel_fro
+from workloads import CONFIGS, make_mask, make_tensors, make_upstream
+
+pytestmark = pytest.mark.gpu
+
+TOL_LP = 5e-3
+TOL_GRAD = 1e-2
+MAX_GAP = 128
+TILE_M = 128
+
+
+def _sample_tokens(mask, n=256, seed=0):
+    T = len(mask)
+    rng = np.random.default_rng(seed)
+    picks = {0, T - 1}
+    for t in (TILE_M - 1, TILE_M, 2 * TILE_M - 1, 2 * TILE_M, T - TILE_M - 1, T - TILE_M):
+        if 0 <= t < T:
+            picks.add(t)
+    for s, e in S.active_spans(mask, MAX_GAP)[:24]:
+        picks.update({s, e - 1, max(s - 1, 0), min(e, T - 1)})
+    act = np.nonzero(mask)[0]
+    if len(act):
+        picks.update(int(x) for x in rng.choice(act, size=min(len(act), n // 2), replace=False))
+    picks.update(int(x) for x in rng.integers(0, T, size=n))
+    return np.array(sorted(picks)[:n], dtype=np.int64)
+
+
+def _slice_window(mask, L):
+    """A window of L tokens whose active fraction is closest to one half."""
+    T = len(mask)
+    c = np.concatenate([[0], np.cumsum(mask, dtype=np.int64)])
+    starts = np.arange(0, T - L + 1, 64)
+    frac = (c[starts + L] - c[starts]) / L
+    return int(starts[np.argmin(np.abs(frac - 0.5))])
+
+
+FULL = [(2, None), (3, None), (4, None), (5, 0.5)]
+
+
+@pytest.mark.parametrize("cid,frac", FULL)
+def test_full_size_spot_checks(cid, frac):
+    cfg = CONFIGS[cid]
+    dev = cuda_device()
+    mask, _ = make_mask(cid, active_frac=frac)
+    T, H, V = cfg.T, cfg.H, cfg.V
+    announce(f"full size config {cid} T={T} H={H} V={V} split={cfg.vocab_split} active={mask.mean():.3f}")
+    h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
+    a, b = make_upstream(mask)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward(h, W, y)
+    dH, dW = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                          m_dev, meta, cfg.vocab_split)
+    torch.cuda.synchronize()
+
+    # active metadata: bit-exact
+    assert meta.host_spans() == S.active_spans(mask, MAX_GAP)
+    assert int(meta.active_count.item()) == int(mask.sum())
+    bits = meta.tile_bits.cpu().numpy().view(np.uint32)
+    ref_bits = S.tile_bits(mask, TILE_M)
+    assert np.array_equal(bits[:len(ref_bits)], ref_bits)
+
+    # forward and d_hidden rows on sampled tokens
+    rows = _sample_tokens(mask, seed=cid)
+    Wf = host64(W)
+    hr = host64(h[torch.as_tensor(rows, device=dev)])
+    yr = y.cpu().numpy()[rows]
+    olp, oent, olse = O.forward(hr, Wf, yr)
+    assert max_abs(lp.cpu().numpy()[rows], olp) <= TOL_LP
+    assert max_abs(ent.cpu().numpy()[rows], oent) <= TOL_LP
+    assert max_abs(lse.cpu().numpy()[rows], olse) <= TOL_LP
+    act = rows[mask[rows] != 0]
+    if len(act):
+        sel = np.searchsorted(rows, act)
+        odH = O.dhidden_rows(hr[sel], Wf, yr[sel], mask[act], a[act], b[act], range(len(act)))
+        gdH = host64(dH[torch.as_tensor(act, device=dev)])
+        assert rel_fro(gdH, odH) <= TOL_GRAD, rel_fro(gdH, odH)
+    del Wf
+
+    # every inactive d_hidden row is bitwise +0
+    inactive = torch.as_tensor(mask == 0, device=dev)
+    raw = dH.view(torch.int16)
+    assert not bool((raw[inactive] != 0).any()), "inactive d_hidden rows must be bitwise +0"
+
+    # d_weight identities, evaluated in fp64 on the device from the stored outputs
+    dW64 = dW.double()
+    col_sum = dW64.sum(dim=0)
+    col_abs = dW64.abs().sum(dim=0)
+    assert float((col_sum.abs() / col_abs.clamp_min(1e-300)).max()) <= 1e-2
+    lhs = float((dH.double() * h.double()).sum())
+    rhs = float((dW64 * W.double()).sum())
+    assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs)), (lhs, rhs)
+    del dW64, dH, dW, h, W
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cid,frac", [(3, None), (4, None), (5, 0.25)])
+def test_full_hv_t_slice_against_oracle(cid, frac):
+    cfg = CONFIGS[cid]
+    dev = cuda_device()
+    L = 1024
+    mask_full, _ = make_mask(cid, active_frac=frac)
+    t0 = _slice_window(mask_full, L)
+    mask = np.ascontiguousarray(mask_full[t0:t0 + L])
+    announce(f"T-slice config {cid} tokens [{t0}, {t0 + L}) H={cfg.H} V={cfg.V} active={mask.mean():.3f}")
+    h_full, W, y_full = make_tensors(cfg.T, cfg.H, cfg.V, cfg.dtype, cfg.seed, device=dev)
+    h = h_full[t0:t0 + L].contiguous()
+    y = y_full[t0:t0 + L].contiguous()
+    del h_full, y_full
+    a, b = make_upstream(mask)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward(h, W, y)
+    dH, dW = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                          m_dev, meta, cfg.vocab_split)
+    torch.cuda.synchronize()
+    hh, WW, yy = host64(h), host64(W), y.cpu().numpy()
+    olp, oent, olse = O.forward(hh, WW, yy)
+    assert max_abs(lp.cpu().numpy(), olp) <= TOL_LP
+    assert max_abs(ent.cpu().numpy(), oent) <= TOL_LP
+    assert max_abs(lse.cpu().numpy(), olse) <= TOL_LP
+    odH, odW = O.backward(hh, WW, yy, mask, a, b)
+    assert rel_fro(host64(dH), odH) <= TOL_GRAD
+    assert rel_fro(host64(dW), odW) <= TOL_GRAD
+    raw = dH.view(torch.int16).cpu().numpy()
+    assert not raw[mask == 0].any()
+    del dH, dW, W, h
+    torch.cuda.empty_cache()
