@@ -47,7 +47,81 @@ def parse():
     p.add_argument("--no-trace", action="store_true")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="run one device copy of this many MiB first (counter calibration)")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the headline run: backward time of the stress workload at its "
+                        "active fractions, fitted against the active-tile fraction")
     return p.parse_args()
+
+
+def method_work(meta, T):
+    """(T_at, T_sp, spans) from the device-built active metadata: tokens in active
+    128-token tiles (tile bitmap) and tokens inside spans (span list)."""
+    tm = int(meta.tile_m)
+    n_tiles = -(-T // tm)
+    words = meta.tile_bits.cpu().numpy().view(np.uint32)
+    idx = np.arange(n_tiles)
+    active = (words[idx >> 5] >> (idx & 31).astype(np.uint32)) & 1
+    sizes = np.minimum(tm, T - idx * tm)
+    spans = meta.host_spans()
+    return int((active * sizes).sum()), int(sum(e - s for s, e in spans)), spans
+
+
+def sweep(args):
+    """Backward time vs active fraction on the stress workload (config 5): one line with
+    every point and the least-squares fit t_bwd = alpha + beta (T_at + T_sp) / T."""
+    import torch
+
+    from entropy_block_sparse_amd import flh_backward, flh_forward, flh_spans_build, flh_workspace_bytes
+    from workloads import get_config, make_mask, make_tensors, make_upstream
+
+    cfg = get_config(5)
+    dev = torch.device("cuda:0")
+    T, H, V, Ssplit = cfg.T, cfg.H, cfg.V, cfg.vocab_split
+    h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
+    ws_f = torch.empty(flh_workspace_bytes(1, h.dtype, T, H, V), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(flh_workspace_bytes(2, h.dtype, T, H, V, Ssplit), dtype=torch.uint8, device=dev)
+    points = []
+    runs = [(f, False) for f in cfg.sweep] + [(1.0, True)]
+    for frac, dense in runs:
+        mask_np, minfo = make_mask(5, active_frac=frac)
+        a_np, b_np = make_upstream(mask_np)
+        mask = torch.as_tensor(mask_np).to(dev)
+        g_lp, g_ent = torch.as_tensor(a_np).to(dev), torch.as_tensor(b_np).to(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t_f, t_b = [], []
+        for it in range(args.warmup + args.steps):
+            ev[0].record()
+            meta = None if dense else flh_spans_build(mask)
+            lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
+            ev[1].record()
+            flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                t_f.append(ev[0].elapsed_time(ev[1]))
+                t_b.append(ev[1].elapsed_time(ev[2]))
+        T_at, T_sp, spans = method_work(flh_spans_build(mask), T)
+        points.append({"active_frac": minfo["active_frac"], "dense_fallback": dense, "spans": len(spans),
+                       "T_at128_frac": T_at / T, "T_sp_frac": T_sp / T,
+                       "x": (T_at + T_sp) / T, "fwd_ms": float(np.median(t_f)),
+                       "bwd_ms": float(np.median(t_b)), "bwd_ms_min": float(np.min(t_b))})
+        print(f"[sweep] f={frac} dense={dense}: fwd {points[-1]['fwd_ms']:.1f} ms, "
+              f"bwd {points[-1]['bwd_ms']:.1f} ms, x={points[-1]['x']:.3f}", file=sys.stderr, flush=True)
+    fit_pts = [p for p in points if not p["dense_fallback"]]
+    x = np.array([p["x"] for p in fit_pts])
+    t = np.array([p["bwd_ms"] for p in fit_pts])
+    A_ = np.stack([np.ones_like(x), x], axis=1)
+    (alpha, beta), *_ = np.linalg.lstsq(A_, t, rcond=None)
+    pred = alpha + beta * x
+    r2 = 1.0 - float(((t - pred) ** 2).sum() / max(((t - t.mean()) ** 2).sum(), 1e-30))
+    out = {"metric": "stress-workload backward time vs active-tile fraction", "unit": "ms",
+           "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "dtype": cfg.dtype, "data": "synthetic",
+           "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit},
+           "points": points,
+           "fit": {"model": "t_bwd = alpha + beta * (T_at + T_sp) / T", "alpha_ms": float(alpha),
+                   "beta_ms": float(beta), "r2": r2}}
+    print(json.dumps(out))
 
 
 def kernel_source_sha() -> str:
@@ -97,11 +171,13 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
     import torch
 
     from entropy_block_sparse_amd import (flh_backward, flh_forward, flh_spans_build,
                                           flh_workspace_bytes, trace_begin, trace_end)
-    from oracle import spans as S
     from workloads import get_config, make_mask, make_tensors, make_upstream
 
     cfg = get_config(args.config)
@@ -150,10 +226,7 @@ def main():
     recs = trace_end(64 * args.steps + 64) if trace else []
 
     # ---- algorithmic work of the method ----
-    flags = S.tile_flags(mask_np, 128)
-    T_at = sum(flags) * 128 - (128 * len(flags) - T if flags and flags[-1] else 0)
-    spans = S.active_spans(mask_np, 128)
-    T_sp = sum(e - s for s, e in spans)
+    T_at, T_sp, spans = method_work(flh_spans_build(mask), T)
     A = int(mask_np.sum())
     pass_flops = 2.0 * H * V
     F_method = pass_flops * (T + T_at + T_sp + T) if not args.dense else pass_flops * 4 * T
