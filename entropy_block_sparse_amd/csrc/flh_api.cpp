@@ -74,8 +74,9 @@ struct BwdLayout {
 BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   BwdLayout L{};
   const int64_t n_skip = cdiv(T, kSkipTile);
-  // every span holds >= 1 token and spans are >= 1 token apart: <= ceil(T/2) spans
-  L.span_tile_cap = cdiv(T, kSpanTile) + (T + 1) / 2 + 1;
+  // span pieces: every span holds >= 1 token and spans are >= 1 token apart, so there
+  // are <= ceil(T/2) spans and <= T/kSpanPiece + (number of spans) pieces
+  L.span_tile_cap = cdiv(T, kSpanPiece) + (T + 1) / 2 + 1;
   const int64_t w_max = V < S ? V : S;
   const int64_t ld_max = pad_ld(w_max);
   L.ld_wt = pad_ld(w_max);
@@ -321,7 +322,8 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
     });
     if (s != FLH_OK) return s;
     s = run(kIdDhidden, tag, st, [&] {
-      return launch_gemm((int)dt, kDhidden, a, grid_for(L.span_tile_cap * h_tiles, cus), st);
+      return launch_gemm((int)dt, kDhidden, a, grid_for(cdiv(L.span_tile_cap, kPiecesPerTile) * h_tiles, cus),
+                         st);
     });
     if (s != FLH_OK) return s;
     s = run(kIdDweight, tag, st, [&] {

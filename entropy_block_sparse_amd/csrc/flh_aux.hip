@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
     run_i += tot_i;
   }
 
-  // span-local row tiles of at most kSpanTile rows, starting at each span start
+  // span pieces of at most kSpanPiece rows, starting at each span start (span order)
   int64_t ns = spans ? (int64_t)(*num_spans) : 1;
   if (spans && ns > span_cap) ns = span_cap;
   int64_t run = 0;
@@ -206,23 +206,25 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
         e = T;
       }
     }
-    const int64_t ntl = (e > s) ? (e - s + kSpanTile - 1) / kSpanTile : 0;
+    const int64_t ntl = (e > s) ? (e - s + kSpanPiece - 1) / kSpanPiece : 0;
     const int64_t incl = block_scan(ntl, sh, AddOp());
     const int64_t tot = sh[kBlock - 1];
     __syncthreads();
     for (int64_t j = 0; j < ntl; ++j) {
       const int64_t idx = run + incl - ntl + j;
       if (idx < span_tile_cap) {
-        const int64_t r0 = s + j * kSpanTile;
+        const int64_t r0 = s + j * kSpanPiece;
         span_tiles[2 * idx] = (int32_t)r0;
-        span_tiles[2 * idx + 1] = (int32_t)((r0 + kSpanTile < e) ? r0 + kSpanTile : e);
+        span_tiles[2 * idx + 1] = (int32_t)((r0 + kSpanPiece < e) ? r0 + kSpanPiece : e);
       }
     }
     run += tot;
   }
   if (tid == 0) {
     counts[0] = (int32_t)n_act;
-    counts[1] = (int32_t)(run < span_tile_cap ? run : span_tile_cap);
+    const int64_t pieces = run < span_tile_cap ? run : span_tile_cap;
+    counts[1] = (int32_t)((pieces + kPiecesPerTile - 1) / kPiecesPerTile);  // hidden-gradient tiles
+    counts[2] = (int32_t)pieces;
   }
 }
 

@@ -153,15 +153,54 @@ __device__ __forceinline__ void group_map(int64_t L, int64_t m_tiles, int64_t n_
   ni = r / gm;
 }
 
-// One operand tile: 256 rows with K contiguous, ldb bytes apart.  Tile rows [0,128)
-// start at base0 (n0 >= 1 valid rows), rows [128,256) at base1 (n1 valid rows, none
-// if n1 <= 0).  The tile starts `trim` bytes into its first memory row; the
-// readable range of each half ends with its last valid row.
+// One operand tile: 256 rows with K contiguous, ldb bytes apart, in eight segments of
+// 32 rows: tile rows [32 j, 32 j + 32) are segment j, whose n (0..32) memory rows start
+// at base; tile rows past n read as zero.  Wave w loads segments 2w and 2w+1.  Either
+// the tile is two halves, rows [0, 128) the first n0 (<= 128) rows at b0 and rows
+// [128, 256) the first n1 rows at b1; or (`pieces` set) segment j is span piece p0 + j
+// of the table of (first, end) token pairs, rows of b0, and empty past n_pieces.
+// Segments are computed, not stored: an array indexed by the wave number would be
+// spilled to scratch memory.
 struct RowSrc {
-  const char *base0;
-  const char *base1;
-  int64_t n0, n1, ldb, trim;
+  const char *b0, *b1;
+  int64_t n0, n1, ldb;
+  const int32_t *pieces;
+  int64_t p0, n_pieces;
 };
+// n_rows consecutive rows from b
+__device__ __forceinline__ RowSrc rows_of(const char *b, int64_t n_rows, int64_t ldb) {
+  const int64_t n0 = n_rows < 128 ? n_rows : 128;
+  return RowSrc{b, b + 128 * ldb, n0, n_rows - n0, ldb, nullptr, 0, 0};
+}
+// tile rows [0, 128) from b0 (n0 rows), [128, 256) from b1 (n1 rows)
+__device__ __forceinline__ RowSrc rows_of2(const char *b0, int64_t n0, const char *b1, int64_t n1,
+                                           int64_t ldb) {
+  return RowSrc{b0, b1, n0 < 128 ? n0 : 128, n1 < 128 ? n1 : 128, ldb, nullptr, 0, 0};
+}
+// first token and length of span piece pc (no rows past the last piece)
+__device__ __forceinline__ void piece(const int32_t *pieces, int64_t pc, int64_t n_pieces, int64_t &start,
+                                      int64_t &len) {
+  start = 0;
+  len = 0;
+  if (pc < n_pieces) {
+    start = uni(pieces[2 * pc]);
+    len = uni(pieces[2 * pc + 1]) - start;
+  }
+}
+// segment j (wave-uniform) of a tile; kPieces says which form s has
+template <bool kPieces>
+__device__ __forceinline__ void seg(const RowSrc &s, int j, const char *&base, int64_t &n) {
+  if constexpr (kPieces) {
+    int64_t st;
+    piece(s.pieces, s.p0 + j, s.n_pieces, st, n);
+    base = s.b0 + st * s.ldb;
+  } else {
+    const bool h1 = j >= 4;
+    const int64_t r = 32 * (j & 3), nh = (h1 ? s.n1 : s.n0) - r;
+    base = (h1 ? s.b1 : s.b0) + r * s.ldb;
+    n = nh < 0 ? 0 : (nh > 32 ? 32 : nh);
+  }
+}
 
 template <typename T, int KIND>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
@@ -268,42 +307,38 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     int64_t mi, ni;
     group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : 8, mi, ni);
 
-    int64_t span_s0 = 0, span_s1 = 0;
-    if constexpr (KIND == kDhidden) {
-      span_s0 = uni(a.span_tiles[2 * mi]);
-      span_s1 = uni(a.span_tiles[2 * mi + 1]);
-    }
-
     // ---------------- operand rows ----------------
     RowSrc srcA, srcB;
     if constexpr (KIND == kFwd) {
       const int64_t v0 = mi * kTile, t0 = ni * kTile, ldb = a.H * kEsz;
-      srcA = RowSrc{Wp + v0 * ldb, Wp + (v0 + 128) * ldb, imin(a.V - v0, 128), a.V - v0 - 128, ldb, 0};
-      srcB = RowSrc{hp + t0 * ldb, hp + (t0 + 128) * ldb, imin(a.T - t0, 128), a.T - t0 - 128, ldb, 0};
+      srcA = rows_of(Wp + v0 * ldb, a.V - v0, ldb);
+      srcB = rows_of(hp + t0 * ldb, a.T - t0, ldb);
     } else if constexpr (KIND == kDlogits) {
       const int64_t v0 = mi * kTile, ldb = a.H * kEsz;
       const char *wb = Wp + (a.v_base + v0) * ldb;
-      srcA = RowSrc{wb, wb + 128 * ldb, imin(a.Ws - v0, 128), a.Ws - v0 - 128, ldb, 0};
+      srcA = rows_of(wb, a.Ws - v0, ldb);
       const int64_t e1 = 2 * ni + 1;
       const int64_t tile0 = uni(a.tile_list[2 * ni]);
       const int64_t tile1 = (e1 < a.n_skip_tiles) ? uni(a.tile_list[e1]) : -1;
-      srcB = RowSrc{hp + tile0 * kSkipTile * ldb, hp + (tile1 >= 0 ? tile1 : tile0) * kSkipTile * ldb,
-                    imin(a.T - tile0 * kSkipTile, 128),
-                    tile1 >= 0 ? imin(a.T - tile1 * kSkipTile, 128) : 0, ldb, 0};
+      srcB = rows_of2(hp + tile0 * kSkipTile * ldb, a.T - tile0 * kSkipTile,
+                      hp + (tile1 >= 0 ? tile1 : tile0) * kSkipTile * ldb,
+                      tile1 >= 0 ? a.T - tile1 * kSkipTile : 0, ldb);
     } else if constexpr (KIND == kDhidden) {
-      const int64_t ldb = (int64_t)a.ld_d * kEsz, nr = span_s1 - span_s0;
-      srcA = RowSrc{Dp + span_s0 * ldb, Dp + (span_s0 + 128) * ldb, imin(nr, 128), nr - 128, ldb, 0};
+      // the tile's eight 32-row segments are span pieces 8 mi .. 8 mi + 7 (a piece is at
+      // most 32 consecutive rows of one span) of the token-major staging
+      const int64_t ldb = (int64_t)a.ld_d * kEsz;
+      srcA = RowSrc{Dp, Dp, 0, 0, ldb, a.span_tiles, 8 * mi, uni(a.counts[2])};
       // rows n (hidden units) of this split's block of W^T
       const int64_t n0 = ni * kTile, ldw = a.ld_wt * kEsz;
       const char *wt = reinterpret_cast<const char *>(a.Wt) + n0 * ldw;
-      srcB = RowSrc{wt, wt + 128 * ldw, imin(a.H - n0, 128), a.H - n0 - 128, ldw, 0};
+      srcB = rows_of(wt, a.H - n0, ldw);
     } else {
       // vocabulary-major staging rows v and h^T rows n, both over all tokens
       const int64_t v0 = mi * kTile, n0 = ni * kTile, ldt = a.ld_t * kEsz;
       const char *dt = reinterpret_cast<const char *>(a.Dt) + v0 * ldt;
       const char *ht = reinterpret_cast<const char *>(a.ht) + n0 * ldt;
-      srcA = RowSrc{dt, dt + 128 * ldt, imin(a.Ws - v0, 128), a.Ws - v0 - 128, ldt, 0};
-      srcB = RowSrc{ht, ht + 128 * ldt, imin(a.H - n0, 128), a.H - n0 - 128, ldt, 0};
+      srcA = rows_of(dt, a.Ws - v0, ldt);
+      srcB = rows_of(ht, a.H - n0, ldt);
     }
 
     f32x16 acc[4][4];
@@ -318,20 +353,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // the accumulators from it, so the epilogue is a plain store.  (The bf16 epilogue
       // adds the earlier sum while it stores.)
       if (!a.first_split) {
-        const int n_rows = (int)(span_s1 - span_s0);
         const int64_t n_tile = ni * kTile;
         const int n_cols = (int)imin(a.H - n_tile, kTile);
-        const float *base = a.dh_acc + span_s0 * a.H + n_tile;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = wm * 128 + (g << 2) + i * 32 + ((r >> 2) << 3) + (r & 3);
-            const float *prow = base + (uint32_t)(row < n_rows ? row : 0) * (uint32_t)a.H;
+            // row wm * 128 + 32 i + lr of the tile: row lr of piece 4 wm + i
+            const int lr = (g << 2) + ((r >> 2) << 3) + (r & 3);
+            int64_t pst, pln;
+            piece(a.span_tiles, 8 * mi + 4 * wm + i, uni(a.counts[2]), pst, pln);
+            const bool ok = lr < pln;
+            const float *prow = a.dh_acc + (ok ? pst + lr : 0) * a.H + n_tile;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int col = wn * 128 + (lane & 31) + j * 32;
-              acc[i][j][r] = (row < n_rows && col < n_cols) ? prow[col] : 0.f;
+              acc[i][j][r] = (ok && col < n_cols) ? prow[col] : 0.f;
             }
           }
       }
@@ -346,33 +383,40 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // an operand's end are clamped onto its last valid row: their products reach
       // only outputs that are never stored.
       const int r_base = tid >> 3;
-      auto offsets = [&](const RowSrc &s, uint32_t (&off)[8], const char *(&bp)[2]) {
-        const bool has1 = s.n1 > 0;
-        bp[0] = s.base0;
-        bp[1] = has1 ? s.base1 : s.base0;
+      // (tile row r_base + 32 i is row r_base of segment i; an empty segment reads
+      // segment 0's first row)
+      auto offsets = [&](auto pieces, const RowSrc &s, uint32_t (&off)[8], const char *(&bp)[8]) {
+        const char *b_first;
+        int64_t n_first;
+        seg<decltype(pieces)::value>(s, 0, b_first, n_first);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int64_t nv = (i < 4 || !has1) ? s.n0 : s.n1;
-          int64_t lr = (i < 4 || !has1) ? (r_base + 32 * (i & 3)) : (r_base + 32 * (i - 4));
-          lr = lr < nv - 1 ? lr : nv - 1;
+          const char *bi;
+          int64_t ni_;
+          seg<decltype(pieces)::value>(s, i, bi, ni_);
+          const bool has = ni_ > 0;
+          int64_t lr = has ? r_base : 0;
+          const int64_t nsg = has ? ni_ : n_first;
+          lr = lr < nsg - 1 ? lr : nsg - 1;
+          bp[i] = has ? bi : b_first;
           off[i] = (uint32_t)(lr * s.ldb + (tid & 7) * 16);
         }
       };
       uint32_t a_off[8], b_off[8];
-      const char *a_bp[2], *b_bp[2];
-      offsets(srcA, a_off, a_bp);
-      offsets(srcB, b_off, b_bp);
+      const char *a_bp[8], *b_bp[8];
+      offsets(std::integral_constant<bool, KIND == kDhidden>{}, srcA, a_off, a_bp);
+      offsets(std::false_type{}, srcB, b_off, b_bp);
       // this thread's chunk of K stage kt lies (at least partly) inside K
       auto chunk_in = [&](int kt) -> bool {
         return !(has_tail && kt == nk - 1) || ((int64_t)kt * kBK + (tid & 7) * kPer < K);
       };
-      auto load_rows = [&](const char *const (&bp)[2], const uint32_t (&off)[8], int kt, u32x4 (&reg)[8]) {
+      auto load_rows = [&](const char *const (&bp)[8], const uint32_t (&off)[8], int kt, u32x4 (&reg)[8]) {
         uint32_t kb = (uint32_t)kt * 128u;
         // a chunk wholly past K reads the (in-row) chunk holding element K - 1 instead
         if (!chunk_in(kt)) kb = (uint32_t)(((K - 1) / kPer) * kPer * kEsz) - (tid & 7) * 16;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          reg[i] = *reinterpret_cast<const u32x4 *>(bp[i < 4 ? 0 : 1] + (uint32_t)(off[i] + kb));
+          reg[i] = *reinterpret_cast<const u32x4 *>(bp[i] + (uint32_t)(off[i] + kb));
       };
       auto store_rows = [&](char *dst, const u32x4 (&reg)[8], int kt) {
         const bool z = !chunk_in(kt);
@@ -439,26 +483,42 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, (int)n, 0x00020000);
       };
-      // Wave w loads tile rows [64 w, 64 w + 64) (waves 0, 1 from half 0, waves 2, 3
-      // from half 1); its load instruction k (0..7) covers rows 64 w + 8 k .. + 7.
+      // Wave w loads tile rows [64 w, 64 w + 64), segments 2w and 2w+1 of the operand; its
+      // load instruction k (0..7) covers rows 64 w + 8 k .. + 7, of segment 2w + k / 4.
       auto load_row = [&](int k) { return 64 * wave + 8 * k + (lane >> 3); };
       auto load_chunk = [&](int k) { return (lane & 7) ^ swz(load_row(k)); };
-      __amdgpu_buffer_rsrc_t ra, rb;
+      // A wave's two segments are contiguous in memory for every operand except the
+      // hidden-gradient staging rows (span pieces), so only that one takes a descriptor
+      // per segment; the others take one per wave (scalar registers are at their limit).
+      constexpr bool kSplitA = KIND == kDhidden;
+      // (separate variables: the host compiler rejects arrays of the descriptor type)
+      __amdgpu_buffer_rsrc_t ra0, ra1, rb;
       uint32_t a_vo[8], b_vo[8];  // per load instruction: this lane's byte offset at k = 0
-      auto setup = [&](const RowSrc &s, __amdgpu_buffer_rsrc_t &r, uint32_t (&vo)[8]) {
-        const bool h1 = (wave >> 1) != 0;
-        const int64_t n = h1 ? s.n1 : s.n0;
-        r = rsrc(uni(h1 ? s.base1 : s.base0), uni(n > 0 ? n * s.ldb - s.trim : 0));
+      auto setup = [&](auto split, const RowSrc &s, __amdgpu_buffer_rsrc_t &r0, __amdgpu_buffer_rsrc_t &r1,
+                       uint32_t (&vo)[8]) {
+        constexpr bool kSplit = decltype(split)::value;
+        const char *b0, *b1;
+        int64_t n0, n1;
+        seg<kSplit>(s, 2 * wave, b0, n0);
+        seg<kSplit>(s, 2 * wave + 1, b1, n1);
+        if (kSplit) {
+          r0 = rsrc(uni(b0), uni(n0 * s.ldb));
+          r1 = rsrc(uni(b1), uni(n1 * s.ldb));
+        } else {
+          r0 = rsrc(uni(b0), uni((n0 + n1) * s.ldb));
+          r1 = r0;
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          vo[k] = (uint32_t)((int64_t)(load_row(k) & 127) * s.ldb) + (uint32_t)(load_chunk(k) * 16);
+          vo[k] = (uint32_t)((int64_t)(load_row(k) & (kSplit ? 31 : 63)) * s.ldb) + (uint32_t)(load_chunk(k) * 16);
       };
-      setup(srcA, ra, a_vo);
-      setup(srcB, rb, b_vo);
+      setup(std::integral_constant<bool, kSplitA>{}, srcA, ra0, ra1, a_vo);
+      setup(std::false_type{}, srcB, rb, rb, b_vo);
       // load k (0..7) of operand op (0 = A, 1 = B) of stage s
       auto issue_one = [&](int s, int op, int k) {
         char *lb = smem + (s & 1) * kStage + op * kOpStage + (8 * wave + k) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, lb, 16, op ? b_vo[k] : a_vo[k], s * 128, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : (kSplitA && k >= 4 ? ra1 : ra0), lb, 16,
+                                                 op ? b_vo[k] : a_vo[k], s * 128, 0, 0);
       };
       // L2 prefetch.  The 32 workgroups of an XCD hold an 8 x 4 block of tiles and share
       // operand rows through its L2; a line a stage needs that no sharer has fetched yet
@@ -470,23 +530,31 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // corner of LDS.  The load
       // goes out after the stage's real loads, so the wait for those can leave it in
       // flight (vector loads complete in order).
+      // The forward kernel gains nothing from it and is short of scalar registers, so
+      // it runs without.
       constexpr int kPfAhead = 3;
-      __amdgpu_buffer_rsrc_t rpf;
-      uint32_t pf_vo;
-      {
+      constexpr bool kPrefetch = KIND != kFwd;
+      __amdgpu_buffer_rsrc_t rpf = rsrc(Wp, 0);
+      uint32_t pf_vo = 0;
+      if constexpr (kPrefetch) {
         const bool isA = wave < 2;
-        const RowSrc &src = isA ? srcA : srcB;
-        const int row_u = isA ? 64 * (int)(ni & 3) + 32 * (wave & 1) : 32 * (int)(mi & 7);  // wave-uniform
-        const bool h1 = row_u >= 128;
-        const int64_t n = h1 ? src.n1 : src.n0;
-        rpf = rsrc(uni(h1 ? src.base1 : src.base0), uni(n > 0 ? n * src.ldb - src.trim : 0));
+        // segment of 32 rows to touch, wave-uniform
+        const int sg = isA ? 2 * (int)(ni & 3) + (wave & 1) : (int)(mi & 7);
+        const char *pb_a, *pb_b;
+        int64_t pn_a, pn_b;
+        seg<kSplitA>(srcA, sg, pb_a, pn_a);
+        seg<false>(srcB, sg, pb_b, pn_b);
+        rpf = isA ? rsrc(uni(pb_a), uni(pn_a * srcA.ldb)) : rsrc(uni(pb_b), uni(pn_b * srcB.ldb));
         // lanes 0..31 touch the first 64 bytes of their row's line, lanes 32..63 the rest
-        pf_vo = (uint32_t)((int64_t)((row_u & 127) + (lane & 31)) * src.ldb) + (uint32_t)((lane >> 5) * 64);
+        pf_vo = (uint32_t)((int64_t)(lane & 31) * (isA ? srcA.ldb : srcB.ldb)) + (uint32_t)((lane >> 5) * 64);
       }
-      const __amdgpu_buffer_rsrc_t rnull = rsrc(Wp, 0);
-      auto issue_pf = [&](int s) {  // always issued, so the vmcnt targets are constant
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s < nkv ? rpf : rnull, smem + kPfLds + wave * 256, 4, pf_vo,
-                                                 s * 128, 0, 0);
+      // Issued for every stage, so the vmcnt targets are constant; a stage past K touches
+      // the last stage again (the scalar offset is not range-checked, so it must stay
+      // inside the rows).
+      auto issue_pf = [&](int s) {
+        if constexpr (kPrefetch)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rpf, smem + kPfLds + wave * 256, 4, pf_vo,
+                                                   (s < nkv ? s : nkv - 1) * 128, 0, 0);
       };
       // Last, partial K stage: chunks wholly past K were read from the next row (or
       // as zeros); overwrite them with zeros once this wave's loads of the stage have
@@ -507,6 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       constexpr int kVm0 = 0x0f70;    // s_waitcnt vmcnt(0) only (gfx9 encoding)
       constexpr int kVm1 = 0x0f71;    // vmcnt(1): all but the latest (prefetch) load
       constexpr int kLgkm0 = 0xc07f;  // s_waitcnt lgkmcnt(0) only
+      constexpr int kVmNext = kPrefetch ? kVm1 : kVm0;  // a stage's own loads landed
 
       auto read_frag = [&](const char *op, int wbase, int i, int q) -> u32x4 {
         const int R = wbase + 32 * i + (lane & 31);
@@ -549,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           __builtin_amdgcn_sched_barrier(0);
         }
         if (next) {
-          __builtin_amdgcn_s_waitcnt(kVm1);  // this wave's loads of stage ns have landed
+          __builtin_amdgcn_s_waitcnt(kVmNext);  // this wave's loads of stage ns have landed
           fix_tail(ns);
           __builtin_amdgcn_s_waitcnt(kLgkm0);  // and its reads of this stage are done
           __builtin_amdgcn_s_barrier();
@@ -784,11 +853,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         });
       }
     } else if constexpr (KIND == kDhidden) {
-      const int n_rows = (int)(span_s1 - span_s0);
       const int64_t n_tile = ni * kTile;
       const int n_cols = (int)imin(a.H - n_tile, kTile);
-      float *base = a.dh_acc + span_s0 * a.H + n_tile;
-      const uint32_t ldh = (uint32_t)a.H;
+      float *base = a.dh_acc + n_tile;  // + token * H
       if constexpr (kV2) {
         // fp32 sum over splits through LDS, half a tile at a time: in phase p every wave
         // writes its row blocks i = 2p, 2p+1 as they sit in registers,
@@ -813,27 +880,32 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const int rwm = wave >> 1, rii = wave & 1;  // the row block this wave stores
           const int row_b = rwm * 128 + (2 * p + rii) * 32;
           const int src_b = lds_col + rwm * 65536 + rii * 16384;  // + (g, r) of the row
+          // the block's 32 rows are one span piece: tokens pst .., valid below pln
+          int64_t pst, pln;
+          piece(a.span_tiles, 8 * mi + (row_b >> 5), uni(a.counts[2]), pst, pln);
+          const int n_in = (int)pln;
+          float *bblk = base + pst * a.H;
 #pragma unroll
           for (int k0 = 0; k0 < 32; k0 += 8) {
             float4 prev[8];
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-              const int row = row_b + k0 + kk;
-              const bool ok = !a.first_split && row < n_rows && c4 < n_cols;
-              prev[kk] = ok ? *reinterpret_cast<const float4 *>(base + (uint32_t)row * ldh + c4)
+              const int rr = k0 + kk;
+              const bool ok = !a.first_split && rr < n_in && c4 < n_cols;
+              prev[kk] = ok ? *reinterpret_cast<const float4 *>(bblk + (uint32_t)rr * (uint32_t)a.H + c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-              const int rr = k0 + kk, row = row_b + rr;  // rr = 4 g + 8 (r / 4) + r % 4
+              const int rr = k0 + kk;  // rr = 4 g + 8 (r / 4) + r % 4
               const int src = src_b + (((rr >> 3) & 3) * 4 + (rr & 3)) * 256 + ((rr >> 2) & 1) * 128;
-              if (row < n_rows && c4 < n_cols) {
+              if (rr < n_in && c4 < n_cols) {
                 float4 v = *reinterpret_cast<const float4 *>(smem + src);
                 v.x += prev[kk].x;
                 v.y += prev[kk].y;
                 v.z += prev[kk].z;
                 v.w += prev[kk].w;
-                *reinterpret_cast<float4 *>(base + (uint32_t)row * ldh + c4) = v;
+                *reinterpret_cast<float4 *>(bblk + (uint32_t)rr * (uint32_t)a.H + c4) = v;
               }
             }
           }
@@ -841,18 +913,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          // tile rows wm * 128 + 32 i + .. are piece 4 wm + i
+          int64_t pst, pln;
+          piece(a.span_tiles, 8 * mi + 4 * wm + i, uni(a.counts[2]), pst, pln);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
-            if (row >= n_rows) continue;
-            float *prow = base + (uint32_t)row * ldh;
+            const int lr = (g << 2) + ((r >> 2) << 3) + (r & 3);
+            if (lr >= pln) continue;
+            float *prow = base + (pst + lr) * a.H;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int col = col0 + j * 32;
               if (col < n_cols) prow[col] = acc[i][j][r];
             }
           }
+        }
       }
     } else {
       const int64_t v_tile = mi * kTile;

@@ -13,8 +13,10 @@ constexpr int kTile = 256;
 // Token-tile height of the d-logits skip bitmap; two such tiles form the token
 // side of one d-logits workgroup tile.
 constexpr int kSkipTile = 128;
-// Rows per span-local hidden-gradient tile.
-constexpr int kSpanTile = 256;
+// Span pieces: each span is cut into pieces of at most kSpanPiece consecutive rows; a
+// hidden-gradient tile takes eight consecutive pieces as its eight 32-row segments.
+constexpr int kSpanPiece = 32;
+constexpr int kPiecesPerTile = 8;
 
 enum GemmKind : int {
   kFwd = 0,   // z = W h^T tile + online softmax partials          (K = H)
@@ -42,8 +44,8 @@ struct GemmArgs {
   const uint8_t *mask;     // [T] or null (all active)
   // work lists (backward), device memory
   const int32_t *tile_list;   // token tiles: active ones ascending, then inactive ascending
-  const int32_t *counts;      // [0] active token tiles, [1] span tiles
-  const int32_t *span_tiles;  // [n][2] half-open token rows
+  const int32_t *counts;      // [0] active token tiles, [1] hidden-gradient tiles, [2] span pieces
+  const int32_t *span_tiles;  // span pieces [n][2], half-open token rows
   int32_t n_skip_tiles;       // ceil(T / kSkipTile)
   // outputs / staging
   float *part;             // forward partials [ceil(V/256)][T][4]

@@ -16,7 +16,7 @@ import pytest
 
 from oracle import spans as S
 
-TILE, SKIP, SPAN_TILE = 256, 128, 256
+TILE, SKIP = 256, 128
 tid = np.arange(256)
 lane = tid & 63
 wave = tid >> 6
@@ -55,58 +55,82 @@ def _pick(n, sample):
 
 
 class Src:
-    """An operand tile: rows [0,128) from base0 (n0 valid rows), rows [128,256)
-    from base1 (n1 valid rows, none if n1 <= 0); ldb bytes per row; the tile starts
-    `trim` bytes into its first memory row (byte offsets into `buf`)."""
+    """An operand tile: eight segments of 32 tile rows; segment j is n[j] (0..32) memory
+    rows starting at byte offset base[j] of `buf`, ldb bytes apart.  Wave w loads
+    segments 2w and 2w+1."""
 
-    def __init__(self, buf, base0, n0, base1, n1, ldb, trim=0):
-        assert n0 >= 1
-        self.buf, self.base0, self.n0, self.base1, self.n1 = buf, base0, n0, base1, n1
-        self.ldb, self.trim = ldb, trim
+    def __init__(self, buf, base, n, ldb):
+        assert len(base) == len(n) == 8 and all(0 <= x <= 32 for x in n)
+        self.buf, self.base, self.n, self.ldb = buf, list(base), list(n), ldb
+
+    @classmethod
+    def rows(cls, buf, b, n_rows, ldb):
+        """n_rows consecutive rows from byte offset b."""
+        return cls(buf, [b + 32 * j * ldb for j in range(8)],
+                   [min(max(n_rows - 32 * j, 0), 32) for j in range(8)], ldb)
+
+    @classmethod
+    def rows2(cls, buf, b0, n0, b1, n1, ldb):
+        """tile rows [0, 128) from b0 (n0 rows), [128, 256) from b1 (n1 rows)."""
+        h0, h1 = cls.rows(buf, b0, min(n0, 128), ldb), cls.rows(buf, b1, min(n1, 128), ldb)
+        return cls(buf, h0.base[:4] + h1.base[:4], h0.n[:4] + h1.n[:4], ldb)
 
 
 def load_rows_v1(src, K, esz, what, sample):
-    """fp32 path: thread owns chunk (tid & 7) of tile rows (tid >> 3) + 32 i; rows
-    clamped onto the half's last valid row; a chunk wholly past K reads the in-row
-    chunk holding element K - 1."""
+    """fp32 path: thread owns chunk (tid & 7) of tile rows (tid >> 3) + 32 i, i.e. row
+    tid >> 3 of segment i, clamped onto the segment's last row (an empty segment reads
+    segment 0's first row); a chunk wholly past K reads the in-row chunk holding
+    element K - 1."""
     kper, BK = 16 // esz, 128 // esz
     nk = cdiv(K, BK)
-    has1 = src.n1 > 0
     r_base = tid >> 3
     c = tid & 7
     offs, bases = [], []
     for i in range(8):
-        nv = src.n0 if (i < 4 or not has1) else src.n1
-        lr = np.minimum(r_base + 32 * (i & 3), nv - 1)
+        sg = i if src.n[i] > 0 else 0
+        lr = r_base if sg == i else np.zeros(256, np.int64)
+        lr = np.minimum(lr, src.n[sg] - 1)
         offs.append(lr * src.ldb + c * 16)
-        bases.append(src.base0 if (i < 4 or not has1) else src.base1)
+        bases.append(src.base[sg])
     offs = np.stack(offs)
     assert (offs >= 0).all() and (offs < U32).all()
     for kt in _stages(nk, sample):
         kb = np.full(256, kt * 128, np.int64)
-        inside = np.ones(256, bool)
         if K % BK and kt == nk - 1:
             inside = kt * BK + c * kper < K
             clamp = (((K - 1) // kper) * kper * esz - c * 16) % U32
             kb = np.where(inside, kb, clamp)
-        # every chunk read lies inside its row (after the tile's first `trim` bytes)
+        # every chunk read lies inside its row
         pos = (kb + c * 16) % U32
-        assert (pos + 16 <= src.ldb - src.trim).all(), f"{what} kt={kt}: chunk leaves its row"
+        assert (pos + 16 <= src.ldb).all(), f"{what} kt={kt}: chunk leaves its row"
         for i in range(8):
             rel = (offs[i] + kb) % U32
             src.buf.check(bases[i] + rel, 16, f"{what} kt={kt} i={i}")
 
 
 def rsrc_v2(src, K, what):
-    """bf16 path: every load goes through a descriptor [base, base + n ldb - trim) per
-    half; the hardware returns zeros past it, so the range must lie in the buffer."""
-    for base, n in ((src.base0, src.n0), (src.base1, src.n1)):
-        nb = 0 if n <= 0 else min(n * src.ldb - src.trim, 0xFFFFFFFF)
+    """bf16 path: segment j is loaded through a descriptor [base[j], base[j] + n[j] ldb);
+    the hardware returns zeros past it, so the range must lie in the buffer."""
+    for base, n in zip(src.base, src.n):
+        nb = min(n * src.ldb, 0xFFFFFFFF)
         if nb > 0:
             assert 0 <= base and base + nb <= src.buf.n, \
                 f"{what}: descriptor [{base}, {base + nb}) outside {src.buf.name} ({src.buf.n})"
-    # lane offset (row within the half, chunk) plus the stage offset fits 32 bits
-    assert 127 * src.ldb + 112 + cdiv(K, 64) * 128 < U32, f"{what}: 32-bit offset overflow"
+    # lane offset (row within the segment, chunk) plus the stage offset fits 32 bits
+    assert 31 * src.ldb + 112 + cdiv(K, 64) * 128 < U32, f"{what}: 32-bit offset overflow"
+
+
+PIECE, PIECES_PER_TILE = 32, 8
+
+
+def span_pieces(spans, piece=PIECE):
+    """Host model of the work-list kernel: each span cut into pieces of at most 32 rows,
+    in span order; hidden-gradient tile m takes pieces 8m .. 8m+7."""
+    out = []
+    for s, e in spans:
+        for r in range(s, e, piece):
+            out.append((r, min(e, r + piece)))
+    return out
 
 
 def transpose_model(inp, R, C, out, ld_out, esz, what, block=0):
@@ -199,6 +223,7 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     dW = Buf("dW", V * H * esz)
 
     def loads(src, K, what):
+        assert src.n[0] >= 1, f"{what}: a tile's first segment always has rows"
         if v2:
             rsrc_v2(src, K, what)
         else:
@@ -211,8 +236,8 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     ldb = H * esz
     for mi, ni in itertools.product(_pick(cdiv(V, TILE), sample), _pick(cdiv(T, TILE), sample)):
         v0, t0 = mi * TILE, ni * TILE
-        loads(Src(W, v0 * ldb, min(V - v0, 128), (v0 + 128) * ldb, V - v0 - 128, ldb), H, "fwd A")
-        loads(Src(h, t0 * ldb, min(T - t0, 128), (t0 + 128) * ldb, T - t0 - 128, ldb), H, "fwd B")
+        loads(Src.rows(W, v0 * ldb, V - v0, ldb), H, "fwd A")
+        loads(Src.rows(h, t0 * ldb, T - t0, ldb), H, "fwd B")
         t = t0 + np.arange(256)
         part.check((mi * T + t[t < T]) * 16, 16, "fwd part")
 
@@ -224,7 +249,9 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     n_skip = len(flags)
     tile_list = [i for i, f in enumerate(flags) if f] + [i for i, f in enumerate(flags) if not f]
     n_act = sum(flags)
-    stiles = S.span_tiles(S.active_spans(mask, 128), SPAN_TILE)
+    pieces = span_pieces(S.active_spans(mask, 128))
+    dh_tiles = [pieces[PIECES_PER_TILE * m:PIECES_PER_TILE * (m + 1)]
+                for m in range(cdiv(len(pieces), PIECES_PER_TILE))]
 
     for sp in _pick(cdiv(V, S_split), sample):
         Ws = min(S_split, V - sp * S_split)
@@ -241,11 +268,11 @@ def model(T, H, V, S_split, esz, mask, sample=False):
             n_live, n_cols = min(Ws - v0, TILE), min(w_pad - v0, TILE)
             wb = (v_base + v0) * ldb
             for ni in _pick(n_pairs_gemm, sample):
-                loads(Src(W, wb, min(Ws - v0, 128), wb + 128 * ldb, Ws - v0 - 128, ldb), H, "dlg A")
+                loads(Src.rows(W, wb, Ws - v0, ldb), H, "dlg A")
                 t0 = tile_list[2 * ni]
                 t1 = tile_list[2 * ni + 1] if 2 * ni + 1 < n_skip else -1
-                loads(Src(h, t0 * SKIP * ldb, min(T - t0 * SKIP, 128), (t1 if t1 >= 0 else t0) * SKIP * ldb,
-                          min(T - t1 * SKIP, 128) if t1 >= 0 else 0, ldb), H, "dlg B")
+                loads(Src.rows2(h, t0 * SKIP * ldb, T - t0 * SKIP, (t1 if t1 >= 0 else t0) * SKIP * ldb,
+                                T - t1 * SKIP if t1 >= 0 else 0, ldb), H, "dlg B")
                 pair = (t0, t1)
                 if v2:
                     dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols)
@@ -283,34 +310,43 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                 t = tl * SKIP + vec * kper
                 ok = (tl >= 0) & (v < min(v0 + TILE, Ws)) & (t < t_pad)
                 Dt.check((v[ok] * ld_t + t[ok]) * esz, 16, "dlg zero^T")
-        # ---- dHidden over span tiles: A = staging rows, B = W^T rows from v_base ----
+        # ---- dHidden over tiles of eight span pieces: A = staging rows, B = W^T rows ----
         ldd, ldw = ld_d * esz, ld_wt * esz
-        for (s0, s1), ni in itertools.product([stiles[x] for x in _pick(len(stiles), sample)],
-                                              _pick(cdiv(H, TILE), sample)):
-            nr, n0 = s1 - s0, ni * TILE
-            loads(Src(D, s0 * ldd, min(nr, 128), (s0 + 128) * ldd, nr - 128, ldd), Ws, "dh A")
+        for tp, ni in itertools.product([dh_tiles[x] for x in _pick(len(dh_tiles), sample)],
+                                        _pick(cdiv(H, TILE), sample)):
+            ps = [p[0] for p in tp] + [0] * (PIECES_PER_TILE - len(tp))
+            pn = [p[1] - p[0] for p in tp] + [0] * (PIECES_PER_TILE - len(tp))
+            assert all(1 <= x <= PIECE for x in pn[:len(tp)])
+            n0 = ni * TILE
+            loads(Src(D, [x * ldd for x in ps], pn, ldd), Ws, "dh A")
             wt = (sp * H + n0) * ldw
-            loads(Src(Wt, wt, min(H - n0, 128), wt + 128 * ldw, H - n0 - 128, ldw), Ws, "dh B")
+            loads(Src.rows(Wt, wt, H - n0, ldw), Ws, "dh B")
             if v2:
-                # read-modify-write of whole rows, 16 bytes per lane (4 columns)
+                # read-modify-write of whole rows, 16 bytes per lane (4 columns), per
+                # 32-row block = one piece
                 c4 = lane * 4
                 for p, rr in itertools.product(range(2), range(32)):
-                    row = (wave >> 1) * 128 + (2 * p + (wave & 1)) * 32 + rr
-                    ok = (row < s1 - s0) & (c4 < min(H - n0, TILE))
-                    acc.check(((s0 + row[ok]) * H + n0 + c4[ok]) * 4, 16, "dh rmw")
+                    row_b = (wave >> 1) * 128 + (2 * p + (wave & 1)) * 32
+                    sg = row_b >> 5
+                    tok = np.array([ps[x] for x in sg]) + rr
+                    ok = (rr < np.array([pn[x] for x in sg])) & (c4 < min(H - n0, TILE))
+                    acc.check((tok[ok] * H + n0 + c4[ok]) * 4, 16, "dh rmw")
                 continue
             for i, r in itertools.product(range(4), range(16)):
-                t = s0 + row_q + i * 32 + ((r >> 2) << 3) + (r & 3)
+                row = row_q + i * 32 + ((r >> 2) << 3) + (r & 3)
+                sg, lr = row >> 5, row & 31
+                t = np.array([ps[x] for x in sg]) + lr
+                okr = lr < np.array([pn[x] for x in sg])
                 for j in range(4):
                     n = n0 + col_q + j * 32
-                    ok = (t < s1) & (n < H)
+                    ok = okr & (n < H)
                     acc.check((t[ok] * H + n[ok]) * 4, 4, "dh store")
         # ---- dWeight: A = vocabulary-major staging rows, B = h^T rows ----
         ldt = ld_t * esz
         for mi, ni in itertools.product(_pick(cdiv(Ws, TILE), sample), _pick(cdiv(H, TILE), sample)):
             v0, n0 = mi * TILE, ni * TILE
-            loads(Src(Dt, v0 * ldt, min(Ws - v0, 128), (v0 + 128) * ldt, Ws - v0 - 128, ldt), T, "dw A")
-            loads(Src(ht, n0 * ldt, min(H - n0, 128), (n0 + 128) * ldt, H - n0 - 128, ldt), T, "dw B")
+            loads(Src.rows(Dt, v0 * ldt, Ws - v0, ldt), T, "dw A")
+            loads(Src.rows(ht, n0 * ldt, H - n0, ldt), T, "dw B")
             if v2:
                 # LDS-staged rows, 16-byte stores (8 columns) via transposing reads
                 li, g4 = lane & 15, lane >> 4
@@ -442,3 +478,23 @@ def test_dhidden_staging_map():
         assert src % 16 == 0
         for e in range(4):
             assert written[(p, src + 4 * e)] == (rwm * 128 + (2 * p + rii) * 32 + rr, c4 + e)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_span_pieces_cover_spans_exactly(seed):
+    """The hidden-gradient tiles' pieces cover every span row exactly once, each piece
+    lies inside one span and holds 1..32 rows."""
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 5000))
+    mask = (rng.random(T) < rng.random()).astype(np.uint8)
+    spans = S.active_spans(mask, 128)
+    pieces = span_pieces(spans)
+    covered = np.zeros(T, np.int32)
+    for s0, s1 in pieces:
+        assert 1 <= s1 - s0 <= PIECE
+        assert any(a <= s0 and s1 <= b for a, b in spans)
+        covered[s0:s1] += 1
+    inside = np.zeros(T, np.int32)
+    for a, b in spans:
+        inside[a:b] = 1
+    assert (covered == inside).all()
