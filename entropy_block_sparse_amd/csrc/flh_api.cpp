@@ -233,7 +233,7 @@ flh_status flh_forward(flh_dtype dt, const void *h, const void *W, const int64_t
   flh_status s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwd, a, grid, st); });
   if (s != FLH_OK) return s;
   return run(kIdFwdCombine, -1, st, [&] {
-    return launch_combine(T, V, a.part, targets, logprob, entropy, lse, st);
+    return launch_combine((int)dt, T, H, V, h, W, a.part, targets, logprob, entropy, lse, st);
   });
 }
 

@@ -230,7 +230,6 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
 
 __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int64_t V,
                                                       const float4 *__restrict__ part,
-                                                      const int64_t *__restrict__ targets,
                                                       float *__restrict__ logprob,
                                                       float *__restrict__ entropy,
                                                       float *__restrict__ lse) {
@@ -251,14 +250,54 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int64_t V,
     u = un;
     M = Mn;
   }
-  const int64_t y = targets[t];
   const float ls = __logf(s);
   const float l = M + ls;
-  float zy = __builtin_nanf("");
-  if (y >= 0 && y < V) zy = part[(y / kTile) * T + t].w;
   lse[t] = l;
   entropy[t] = ls - u / s;
-  logprob[t] = zy - l;
+  logprob[t] -= l;  // holds the target's logit z_y (NaN for a target outside [0, V))
+}
+
+// The target's logit z_y = h[t] . W[y_t], one wavefront per token: each lane takes
+// 16-byte chunks of both rows, fp32 products and sums, then a butterfly over the wave.
+// Written to out[t] (NaN for a target outside [0, V)).
+template <typename E>
+__global__ __launch_bounds__(256) void target_logit_kernel(int64_t T, int64_t H, int64_t V,
+                                                           const E *__restrict__ h,
+                                                           const E *__restrict__ W,
+                                                           const int64_t *__restrict__ targets,
+                                                           float *__restrict__ out) {
+  constexpr int kPer = 16 / sizeof(E);
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;  // whole wavefronts
+  const int64_t y = targets[t];
+  if (y < 0 || y >= V) {
+    if (lane == 0) out[t] = __builtin_nanf("");
+    return;
+  }
+  const E *hr = h + t * H;
+  const E *wr = W + y * H;
+  float acc = 0.f;
+  for (int64_t c = (int64_t)lane * kPer; c < H; c += 64 * kPer) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(hr + c);
+    const uint4 w = *reinterpret_cast<const uint4 *>(wr + c);
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc = __builtin_fmaf(__uint_as_float(xs[k] << 16), __uint_as_float(ws[k] << 16), acc);
+        acc = __builtin_fmaf(__uint_as_float(xs[k] & 0xffff0000u), __uint_as_float(ws[k] & 0xffff0000u), acc);
+      }
+    } else {
+      acc = __builtin_fmaf(__uint_as_float(x.x), __uint_as_float(w.x), acc);
+      acc = __builtin_fmaf(__uint_as_float(x.y), __uint_as_float(w.y), acc);
+      acc = __builtin_fmaf(__uint_as_float(x.z), __uint_as_float(w.z), acc);
+      acc = __builtin_fmaf(__uint_as_float(x.w), __uint_as_float(w.w), acc);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) out[t] = acc;
 }
 
 template <typename T>
@@ -314,11 +353,23 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int64_t T, int64_t V, const float *part, const int64_t *targets,
-                          float *logprob, float *entropy, float *lse, hipStream_t st) {
+hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
+                          const float *part, const int64_t *targets, float *logprob, float *entropy,
+                          float *lse, hipStream_t st) {
+  const unsigned tl_blocks = (unsigned)((T + 3) / 4);
+  if (dtype == 1)
+    hipLaunchKernelGGL(target_logit_kernel<uint16_t>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
+                       reinterpret_cast<const uint16_t *>(h), reinterpret_cast<const uint16_t *>(W),
+                       targets, logprob);
+  else
+    hipLaunchKernelGGL(target_logit_kernel<float>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
+                       reinterpret_cast<const float *>(h), reinterpret_cast<const float *>(W), targets,
+                       logprob);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t blocks = (T + 255) / 256;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, T, V,
-                     reinterpret_cast<const float4 *>(part), targets, logprob, entropy, lse);
+                     reinterpret_cast<const float4 *>(part), logprob, entropy, lse);
   return hipGetLastError();
 }
 

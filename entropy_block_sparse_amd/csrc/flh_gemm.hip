@@ -706,55 +706,78 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       }
     };
     if constexpr (KIND == kFwd) {
+      // Per token (column) of the tile: max M of its logits over the tile's vocabulary
+      // rows, s = sum e^(z - M), u = sum e^(z - M) (z - M).  Exponentials are taken in
+      // base 2 (d = (z - M) log2 e, e = 2^d, u = ln 2 * sum e d); each sum runs as four
+      // independent chains (one per row block i), since a single wave per SIMD cannot
+      // hide a long dependent chain.  The target's logit is not picked out here: it is
+      // one dot product per token, taken beside the merge of the tile states.
       const int64_t v_tile = mi * kTile;
       const int n_rows = (int)imin(a.V - v_tile, kTile);  // valid vocabulary rows
-      const bool full = n_rows == kTile;
       const int64_t t_tile = ni * kTile;
+      constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+      // Rows past the vocabulary (last tile only) read as a large finite negative logit:
+      // its exponential is 0 and 0 * d stays 0.  A wave with no valid row at all
+      // reports the empty state instead.  The masked and the plain epilogue are two
+      // instances of one body, so the accumulators are only ever read.
+      const bool wave_live = wm * 128 < n_rows;
+      const int row_lim = n_rows - row0;  // tile row row0 + off is valid iff off < row_lim
       float4 *xch = reinterpret_cast<float4 *>(smem);
-      float st_M[4], st_s[4], st_u[4], st_zy[4];
+      float st_M[4], st_s[4], st_u[4];
+      auto softmax_states = [&](auto masked) {
+        constexpr bool kMasked = decltype(masked)::value;
+        auto z_at = [&](int i, int j, int r) -> float {
+          const float z = acc[i][j][r];
+          if constexpr (kMasked)
+            return i * 32 + ((r >> 2) << 3) + (r & 3) < row_lim ? z : -1.0e30f;
+          else
+            return z;
+        };
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = col0 + j * 32;
-        const int64_t t = t_tile + col;
-        // target row local to this tile, or -1
-        int yl = -1;
-        if (t < a.T) {
-          const int64_t yd = a.targets[t] - v_tile;
-          yl = (yd >= 0 && yd < kTile) ? (int)yd : -1;
-        }
-        float mx = kNegInf;
+        for (int j = 0; j < 4; ++j) {
+          float m4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            m4[i] = z_at(i, j, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
-            if (full || row < n_rows) mx = fmaxf(mx, acc[i][j][r]);
+            for (int r = 1; r < 16; ++r) m4[i] = fmaxf(m4[i], z_at(i, j, r));
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        float s = 0.f, u = 0.f, zy = kNegInf;
+          float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float nm2 = -mx * kLog2e;
+          float s4[4], u4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            s4[i] = 0.f;
+            u4[i] = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
-            const float z = acc[i][j][r];
-            if (full || row < n_rows) {
-              const float d = z - mx;
-              const float e = __expf(d);
-              s += e;
-              u += e * d;
+            for (int r = 0; r < 16; ++r) {
+              const float d = __builtin_fmaf(z_at(i, j, r), kLog2e, nm2);
+              const float e = __builtin_amdgcn_exp2f(d);
+              s4[i] += e;
+              u4[i] = __builtin_fmaf(e, d, u4[i]);
             }
-            if (row == yl) zy = z;
           }
-        s += __shfl_xor(s, 32);
-        u += __shfl_xor(u, 32);
-        zy = fmaxf(zy, __shfl_xor(zy, 32));
-        st_M[j] = mx;
-        st_s[j] = s;
-        st_u[j] = u;
-        st_zy[j] = zy;
-        if (wm == 1 && elane < 32) xch[col] = make_float4(mx, s, u, zy);
-      }
+          float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+          float u = (u4[0] + u4[1]) + (u4[2] + u4[3]);
+          s += __shfl_xor(s, 32);
+          u += __shfl_xor(u, 32);
+          u *= kLn2;
+          if (!wave_live) {
+            mx = kNegInf;
+            s = 0.f;
+            u = 0.f;
+          }
+          st_M[j] = mx;
+          st_s[j] = s;
+          st_u[j] = u;
+          if (wm == 1 && elane < 32) xch[col0 + j * 32] = make_float4(mx, s, u, 0.f);
+        }
+      };
+      if (n_rows < kTile)
+        softmax_states(std::true_type{});
+      else
+        softmax_states(std::false_type{});
       __syncthreads();
       if (wm == 0 && elane < 32) {
         float4 *out = reinterpret_cast<float4 *>(a.part) + mi * a.T + t_tile;
@@ -765,8 +788,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const float4 o = xch[col];
           float M = st_M[j], s = st_s[j], u = st_u[j];
           merge_state(M, s, u, o.x, o.y, o.z);
-          const float zy = fmaxf(st_zy[j], o.w);
-          if (col < n_cols) out[col] = make_float4(M, s, u, zy);
+          if (col < n_cols) out[col] = make_float4(M, s, u, 0.f);
         }
       }
     } else if constexpr (KIND == kDlogits) {

@@ -75,8 +75,11 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
                         int32_t *counts, int32_t *span_tiles, int64_t span_tile_cap,
                         hipStream_t st);
 
-hipError_t launch_combine(int64_t T, int64_t V, const float *part, const int64_t *targets,
-                          float *logprob, float *entropy, float *lse, hipStream_t st);
+// Target logits z_y = h[t] . W[y_t] into logprob, then the merge of the per-tile
+// softmax states into lse, entropy and logprob = z_y - lse.
+hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
+                          const float *part, const int64_t *targets, float *logprob, float *entropy,
+                          float *lse, hipStream_t st);
 
 // Blocked transpose: rows of `in` ([R][C] row-major, elements of esz bytes, 2 or 4)
 // are taken in blocks of `block` rows (a multiple of 64; 0 = one block of R rows);
