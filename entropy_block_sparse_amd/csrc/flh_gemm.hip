@@ -19,19 +19,24 @@
 //             a dense contraction), read from the vocabulary-major staging and h^T.
 //
 // One kernel template serves all four.  A workgroup of 4 waves owns a 256 x 256
-// output tile; each wave a 128 x 128 quadrant as 4 x 4 blocks of 32 x 32 MFMA
+// output tile; each wave a 128 x 128 quadrant as 8 x 8 blocks of 16 x 16 MFMA
 // accumulators.  Every operand is a set of rows with the contraction index K
 // contiguous in memory (h, W, W^T, h^T and the two staging layouts), so there is a
 // single load path.  Workgroups are persistent (grid = compute units) and walk a
 // tile list whose order keeps the tiles of one XCD (workgroup id mod 8) in a
 // compact block, so operand rows are shared in that XCD's L2.
 //
-// bf16 main loop: operands go straight from global memory into a 4-stage LDS ring
-// (buffer_load ... lds, 32 K elements per stage, 3 stages in flight), bounded by
-// buffer descriptors so that rows past an operand's end read as zero; the LDS
-// fragment reads of the next K slice are interleaved with the current slice's
-// v_mfma_f32_32x32x16_bf16.  fp32 main loop (small problems): register-staged
-// loads into two padded LDS stages, four v_mfma_f32_32x32x2_f32 per fragment.
+// bf16 main loop: operands go straight from global memory into two LDS stages of 64
+// K elements (buffer_load ... lds), bounded by buffer descriptors so that rows past
+// an operand's end read as zero; the LDS fragment reads of the next K step are
+// interleaved with the current step's v_mfma_f32_16x16x32_bf16.  fp32 main loop
+// (small problems): register-staged loads into two padded LDS stages, four
+// v_mfma_f32_16x16x4_f32 per fragment.
+//
+// Why 16 x 16 blocks: with random operands the matrix cores run into the chip's power
+// limit, and the 16 x 16 x 32 instruction reads and writes half the accumulator bytes
+// per flop of the 32 x 32 x 16 one; a register-only loop of it sustains a higher clock
+// at the same operand bytes per flop.
 #include <hip/hip_runtime.h>
 
 #include "flh_internal.h"
@@ -40,7 +45,7 @@ namespace flh {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -58,14 +63,19 @@ constexpr int kPfLds = 2 * kStage;                // prefetch scratch: 256 bytes
 // 528 bytes (16-byte aligned, consecutive rows 4 banks apart)
 constexpr int kLsPitch = 528;
 constexpr int kLdsBytesDlg = kTile * kLsPitch > kLdsBytesV2 ? kTile * kLsPitch : kLdsBytesV2;
-// (the bf16 hidden-gradient epilogue stages half a tile of fp32, 128 KiB, in the ring)
+// bf16 hidden-gradient epilogue: half a tile of fp32 staged per wave, 32 groups of
+// 4 x 256 bytes (one row block, one column block) each padded by 64 bytes
+constexpr int kDhGroup = 4 * 256 + 64;
+constexpr int kDhWave = 32 * kDhGroup;
+constexpr int kLdsBytesDh = 4 * kDhWave > kLdsBytesV2 ? 4 * kDhWave : kLdsBytesV2;
 
 // Shared memory of one kernel instantiation: the main loop's stages plus whatever its
 // epilogue stages.
 template <typename T, int KIND>
 constexpr int lds_bytes() {
   return sizeof(T) != 2 ? kLdsBytes
-                        : (KIND == kDlogits || KIND == kDweight ? kLdsBytesDlg : kLdsBytesV2);
+                        : (KIND == kDlogits || KIND == kDweight ? kLdsBytesDlg
+                                                                : (KIND == kDhidden ? kLdsBytesDh : kLdsBytesV2));
 }
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -90,23 +100,38 @@ __device__ __forceinline__ const char *uni(const char *p) {
 }
 
 // ---- matrix-core step: acc += a * b for one 16-byte fragment per lane ---------------
-// Lane l feeds row (l % 32) of A and column (l % 32) of B with the K elements of
-// the 16-byte chunk at position (l / 32) of a 32-byte K slice; A and B use the same
-// lane -> K assignment, so every K element is paired with itself.
+// Lane l feeds row (l % 16) of A and column (l % 16) of B with the K elements of
+// the 16-byte chunk at position (l / 16) of a 64-byte K slice; A and B use the same
+// lane -> K assignment, so every K element is paired with itself.  The 16 x 16
+// result: lane l holds column (l % 16), rows 4 (l / 16) .. + 3.
+//
+// run() is the compiler's builtin, for which the compiler inserts the wait states the
+// matrix-core pipeline requires.  run_in_place() (bf16 main loop) issues the same
+// instruction from inline assembly with the accumulator tied in place: with the
+// builtin, 64 accumulators of 4 registers fill the 256 accumulator registers exactly
+// and the register allocator rotates some of them through spare registers on every
+// stage, which costs moves and wait states in the loop.  The compiler does not track
+// wait states around inline assembly; the bf16 kernels are checked for them on the
+// host after compilation, and the last K stage of every tile uses run() so that the
+// compiler again owns the hazards of the epilogue that reads the accumulators.
 template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {
-  static __device__ __forceinline__ void run(f32x16 &c, u32x4 a, u32x4 b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+  static __device__ __forceinline__ void run(f32x4 &c, u32x4 a, u32x4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void run_in_place(f32x4 &c, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   }
 };
 template <> struct Mma<float> {
-  static __device__ __forceinline__ void run(f32x16 &c, u32x4 a, u32x4 b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  static __device__ __forceinline__ void run(f32x4 &c, u32x4 a, u32x4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ void run_in_place(f32x4 &c, u32x4 a, u32x4 b) { run(c, a, b); }
 };
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -215,7 +240,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1;
   const int wn = wave & 1;
-  const int g = lane >> 5;
 
   // ---------------- extents of this launch ----------------
   int64_t m_tiles, n_tiles, K;
@@ -341,13 +365,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       srcB = rows_of(ht, a.H - n0, ldt);
     }
 
-    f32x16 acc[4][4];
+    // acc[i][j][x]: tile row wm * 128 + 16 i + 4 (lane / 16) + x, tile column
+    // wn * 128 + 16 j + lane % 16
+    f32x4 acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int x = 0; x < 4; ++x) acc[i][j][x] = 0.f;
     if constexpr (KIND == kDhidden && !kV2) {
       // fp32: splits after the first continue the fp32 sum of the earlier splits: start
       // the accumulators from it, so the epilogue is a plain store.  (The bf16 epilogue
@@ -356,21 +382,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t n_tile = ni * kTile;
         const int n_cols = (int)imin(a.H - n_tile, kTile);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i) {
+          // tile rows wm * 128 + 16 i + .. are rows 16 (i % 2) + .. of piece 4 wm + i / 2
+          int64_t pst, pln;
+          piece(a.span_tiles, 8 * mi + 4 * wm + (i >> 1), uni(a.counts[2]), pst, pln);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // row wm * 128 + 32 i + lr of the tile: row lr of piece 4 wm + i
-            const int lr = (g << 2) + ((r >> 2) << 3) + (r & 3);
-            int64_t pst, pln;
-            piece(a.span_tiles, 8 * mi + 4 * wm + i, uni(a.counts[2]), pst, pln);
+          for (int x = 0; x < 4; ++x) {
+            const int lr = 16 * (i & 1) + 4 * (lane >> 4) + x;
             const bool ok = lr < pln;
             const float *prow = a.dh_acc + (ok ? pst + lr : 0) * a.H + n_tile;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int col = wn * 128 + (lane & 31) + j * 32;
-              acc[i][j][r] = (ok && col < n_cols) ? prow[col] : 0.f;
+            for (int j = 0; j < 8; ++j) {
+              const int col = wn * 128 + (lane & 15) + j * 16;
+              acc[i][j][x] = (ok && col < n_cols) ? prow[col] : 0.f;
             }
           }
+        }
       }
     }
 
@@ -435,9 +462,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         store_rows(As, ra, kt);
         store_rows(As + kOpBytes, rb, kt);
       };
-      const int frag_row = lane & 31;
-      const int a_frag = (wm * 128 + frag_row) * kRowBytes + g * 16;
-      const int b_frag = (wn * 128 + frag_row) * kRowBytes + g * 16;
+      const int frag_row = lane & 15;
+      const int a_frag = (wm * 128 + frag_row) * kRowBytes + (lane >> 4) * 16;
+      const int b_frag = (wn * 128 + frag_row) * kRowBytes + (lane >> 4) * 16;
       load_stage(0);
       store_stage(0, 0);
       __syncthreads();
@@ -447,18 +474,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const char *As = smem + st * 2 * kOpBytes;
         const char *Bs = As + kOpBytes;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u32x4 fa[4], fb[4];
+        for (int q = 0; q < 2; ++q) {  // the stage row's two 64-byte K slices
+          u32x4 fa[8], fb[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            fa[i] = *reinterpret_cast<const u32x4 *>(As + a_frag + i * 32 * kRowBytes + q * 32);
+          for (int i = 0; i < 8; ++i)
+            fa[i] = *reinterpret_cast<const u32x4 *>(As + a_frag + i * 16 * kRowBytes + q * 64);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            fb[j] = *reinterpret_cast<const u32x4 *>(Bs + b_frag + j * 32 * kRowBytes + q * 32);
+          for (int j = 0; j < 8; ++j)
+            fb[j] = *reinterpret_cast<const u32x4 *>(Bs + b_frag + j * 16 * kRowBytes + q * 64);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
+            for (int j = 0; j < 8; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
         }
         if (kt + 1 < nk) store_stage(st ^ 1, kt + 1);
         __syncthreads();
@@ -478,7 +505,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int nkv = (int)cdiv(K, kBKv);
       const bool ktail = (K % kBKv) != 0;
       auto swz = [](int r) { return (r >> 1) & 7; };
-      const int swz_lane = swz(lane & 31);  // same for every fragment row of this lane
       auto rsrc = [](const char *base, int64_t bytes) {
         const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, (int)n, 0x00020000);
@@ -577,44 +603,57 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       constexpr int kLgkm0 = 0xc07f;  // s_waitcnt lgkmcnt(0) only
       constexpr int kVmNext = kPrefetch ? kVm1 : kVm0;  // a stage's own loads landed
 
+      // Fragment of block i (16 rows from wbase + 16 i) for K slice q (0, 1: 32 elements,
+      // 64 bytes) of a stage: lane l reads row l % 16, logical chunk 4 q + l / 16.
+      const int swz_lane = swz(lane & 15);  // same for every fragment row of this lane
       auto read_frag = [&](const char *op, int wbase, int i, int q) -> u32x4 {
-        const int R = wbase + 32 * i + (lane & 31);
-        return *reinterpret_cast<const u32x4 *>(op + R * 128 + (((2 * q + g) ^ swz_lane) << 4));
+        const int R = wbase + 16 * i + (lane & 15);
+        return *reinterpret_cast<const u32x4 *>(op + R * 128 + (((4 * q + (lane >> 4)) ^ swz_lane) << 4));
       };
-      // Fragment read p (0..7) of K slice q (0..3, 16 elements each) of stage s, in the
-      // order the MFMAs consume them: A0, B0..B3, A1..A3.
-      auto read_one = [&](int s, int q, int p, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+      // Fragment read p (0..15) of K slice q of stage s, in the order the MFMAs consume
+      // them: A0, B0..B7, A1..A7.
+      auto read_one = [&](int s, int q, int p, u32x4 (&fa)[8], u32x4 (&fb)[8]) {
         const char *lb = smem + (s & 1) * kStage;
         if (p == 0)
           fa[0] = read_frag(lb, wm * 128, 0, q);
-        else if (p < 5)
+        else if (p < 9)
           fb[p - 1] = read_frag(lb + kOpStage, wn * 128, p - 1, q);
         else
-          fa[p - 4] = read_frag(lb, wm * 128, p - 4, q);
+          fa[p - 8] = read_frag(lb, wm * 128, p - 8, q);
       };
-      // One K slice: 16 MFMAs on fragments (ca, cb) in the order (i, j) = (p/4, p%4),
-      // with fragment read p of slice rq of stage rs (into na, nb) beside MFMA p for
-      // p < 8, so the next slice's operands land well before it starts, and, if
-      // ls >= 0, all 16 loads of stage ls (A then B) one per MFMA.  A scheduling fence
-      // after every step keeps exactly this order.
-      auto slice = [&](const u32x4 (&ca)[4], const u32x4 (&cb)[4], u32x4 (&na)[4], u32x4 (&nb)[4],
-                       bool rd, int rs, int rq, int ls, int pfs = -1) {
+      // A stage is two K steps of 64 MFMAs, (i, j) = (p / 8, p % 8) for MFMA p.  A
+      // scheduling fence after every MFMA keeps the order written here.
+      //
+      // First step (fragments ca, cb): beside MFMA 2k + 1 (k < 16) fragment read k of
+      // slice 1 of this stage into (na, nb); beside MFMA 2k, load k of stage ls (if
+      // ls >= 0; A then B); after the last load, the L2 prefetch of stage pfs.
+      // `last`: the tile's last stage, with the compiler's MFMA (see Mma).
+      auto mma = [&](bool last, int p, const u32x4 (&ca)[8], const u32x4 (&cb)[8]) {
+        if (last)
+          Mma<T>::run(acc[p >> 3][p & 7], ca[p >> 3], cb[p & 7]);
+        else
+          Mma<T>::run_in_place(acc[p >> 3][p & 7], ca[p >> 3], cb[p & 7]);
+      };
+      auto kstep0 = [&](const u32x4 (&ca)[8], const u32x4 (&cb)[8], u32x4 (&na)[8], u32x4 (&nb)[8],
+                        int rs, int ls, int pfs, bool last) {
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-          if (rd && p < 8) read_one(rs, rq, p, na, nb);
-          if (ls >= 0) issue_one(ls, p >> 3, p & 7);
-          if (pfs >= 0 && p == 0) issue_pf(pfs);
-          Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
+        for (int p = 0; p < 64; ++p) {
+          if (p < 32 && (p & 1)) read_one(rs, 1, p >> 1, na, nb);
+          if (ls >= 0 && p < 32 && !(p & 1)) issue_one(ls, (p >> 1) >> 3, (p >> 1) & 7);
+          if (pfs >= 0 && p == 32) issue_pf(pfs);
+          mma(last, p, ca, cb);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      // The last slice of stage kt: 8 MFMAs; then, if there is a next stage, wait for
-      // its loads, publish it (barrier) and read its first slice beside the other 8.
-      auto slice_last = [&](const u32x4 (&ca)[4], const u32x4 (&cb)[4], u32x4 (&na)[4], u32x4 (&nb)[4],
-                            bool next, int ns) {
+      // Second step: kBarAt MFMAs; then, if there is a next stage, wait for its loads,
+      // publish it (barrier) and read its slice 0 into (na, nb), one fragment beside
+      // each of the remaining MFMAs.
+      constexpr int kBarAt = 48;
+      auto kstep1 = [&](const u32x4 (&ca)[8], const u32x4 (&cb)[8], u32x4 (&na)[8], u32x4 (&nb)[8],
+                        bool next, int ns) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
+        for (int p = 0; p < kBarAt; ++p) {
+          mma(!next, p, ca, cb);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (next) {
@@ -624,53 +663,56 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           __builtin_amdgcn_s_barrier();
         }
 #pragma unroll
-        for (int p = 8; p < 16; ++p) {
-          if (next) read_one(ns, 0, p - 8, na, nb);
-          Mma<T>::run(acc[p >> 2][p & 3], ca[p >> 2], cb[p & 3]);
+        for (int p = kBarAt; p < 64; ++p) {
+          if (next) {
+            const int r0 = p - kBarAt, nr = 64 - kBarAt;  // reads spread over the rest
+            if (nr >= 16) {
+              if (r0 < 16) read_one(ns, 0, r0, na, nb);
+            } else {
+              for (int r = r0 * 16 / nr; r < (r0 + 1) * 16 / nr; ++r) read_one(ns, 0, r, na, nb);
+            }
+          }
+          mma(!next, p, ca, cb);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
 
-      // ---- prologue: stage 0 loaded and visible, its first slice read ----
+      // ---- prologue: stage 0 loaded and visible, its slice 0 read ----
 #pragma unroll
       for (int k8 = 0; k8 < 16; ++k8) issue_one(0, k8 >> 3, k8 & 7);
       __builtin_amdgcn_s_waitcnt(kVm0);
       fix_tail(0);
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
-      u32x4 F0a[4], F0b[4], F1a[4], F1b[4];
+      u32x4 F0a[8], F0b[8], F1a[8], F1b[8];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) read_one(0, 0, p, F0a, F0b);
+      for (int p = 0; p < 16; ++p) read_one(0, 0, p, F0a, F0b);
       __builtin_amdgcn_sched_barrier(0);
 
       // Stage kt: stage kt+1 streams into the other buffer (which held stage kt-1,
-      // released by the previous barrier) during the first slice; the last slice
+      // released by the previous barrier) during the first step; the second step
       // publishes it.  The last stage is peeled so the loop body is one straight path.
       for (int kt = 0; kt + 1 < nkv; ++kt) {
-        slice(F0a, F0b, F1a, F1b, true, kt, 1, kt + 1);
-        slice(F1a, F1b, F0a, F0b, true, kt, 2, -1, kt + kPfAhead);
-        slice(F0a, F0b, F1a, F1b, true, kt, 3, -1);
-        slice_last(F1a, F1b, F0a, F0b, true, kt + 1);
+        kstep0(F0a, F0b, F1a, F1b, kt, kt + 1, kt + kPfAhead, false);
+        kstep1(F1a, F1b, F0a, F0b, true, kt + 1);
       }
-      slice(F0a, F0b, F1a, F1b, true, nkv - 1, 1, -1);
-      slice(F1a, F1b, F0a, F0b, true, nkv - 1, 2, -1);
-      slice(F0a, F0b, F1a, F1b, true, nkv - 1, 3, -1);
-      slice_last(F1a, F1b, F0a, F0b, false, 0);
+      kstep0(F0a, F0b, F1a, F1b, nkv - 1, -1, -1, true);
+      kstep1(F1a, F1b, F0a, F0b, false, 0);
       __builtin_amdgcn_s_waitcnt(kVm0);  // prefetches still in flight target LDS
       __syncthreads();  // every wave is done with the ring before epilogues reuse LDS
     }
 
     // ---------------- epilogues ----------------
-    // acc[i][j][r] holds tile row  wm*128 + i*32 + 8*(r/4) + 4*g + (r%4)
-    //               and tile col  wn*128 + j*32 + (lane % 32).
+    // acc[i][j][x] holds tile row  wm*128 + i*16 + 4*(lane / 16) + x
+    //               and tile col  wn*128 + j*16 + (lane % 16).
     // Indices below are tile-local 32-bit; tile origins are uniform.
     // Epilogue addresses depend only on the lane; computed from an opaque copy of the
     // lane index here, they cannot be hoisted out of the tile loop and held in
     // registers through the main loop.
     int elane = lane;
     asm volatile("" : "+v"(elane));
-    const int row0 = wm * 128 + ((elane >> 5) << 2);  // + i*32 + 8*(r/4) + (r%4)
-    const int col0 = wn * 128 + (elane & 31);         // + j*32
+    const int row0 = wm * 128 + ((elane >> 4) << 2);  // + i*16 + x
+    const int col0 = wn * 128 + (elane & 15);         // + j*16
     // bf16 epilogues stage a 256 x 256 bf16 tile in LDS column-major, Ls[col][row] with
     // kLsPitch-byte lines (a lane's 4 consecutive rows are one 8-byte write), and write
     // it out row by row with transposing LDS reads: in a group of 16 lanes, lane i
@@ -709,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // Per token (column) of the tile: max M of its logits over the tile's vocabulary
       // rows, s = sum e^(z - M), u = sum e^(z - M) (z - M).  Exponentials are taken in
       // base 2 (d = (z - M) log2 e, e = 2^d, u = ln 2 * sum e d); each sum runs as four
-      // independent chains (one per row block i), since a single wave per SIMD cannot
+      // independent chains (row blocks i and i + 4), since a single wave per SIMD cannot
       // hide a long dependent chain.  The target's logit is not picked out here: it is
       // one dot product per token, taken beside the merge of the tile states.
       const int64_t v_tile = mi * kTile;
@@ -723,43 +765,47 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const bool wave_live = wm * 128 < n_rows;
       const int row_lim = n_rows - row0;  // tile row row0 + off is valid iff off < row_lim
       float4 *xch = reinterpret_cast<float4 *>(smem);
-      float st_M[4], st_s[4], st_u[4];
+      float st_M[8], st_s[8], st_u[8];
       auto softmax_states = [&](auto masked) {
         constexpr bool kMasked = decltype(masked)::value;
-        auto z_at = [&](int i, int j, int r) -> float {
-          const float z = acc[i][j][r];
+        auto z_at = [&](int i, int j, int x) -> float {
+          const float z = acc[i][j][x];
           if constexpr (kMasked)
-            return i * 32 + ((r >> 2) << 3) + (r & 3) < row_lim ? z : -1.0e30f;
+            return i * 16 + x < row_lim ? z : -1.0e30f;
           else
             return z;
         };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
+          // chain c takes row blocks c and c + 4
           float m4[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            m4[i] = z_at(i, j, 0);
+          for (int c = 0; c < 4; ++c) {
+            m4[c] = z_at(c, j, 0);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) m4[i] = fmaxf(m4[i], z_at(i, j, r));
+            for (int e = 1; e < 8; ++e) m4[c] = fmaxf(m4[c], z_at(c + 4 * (e >> 2), j, e & 3));
           }
           float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
           mx = fmaxf(mx, __shfl_xor(mx, 32));
           const float nm2 = -mx * kLog2e;
           float s4[4], u4[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            s4[i] = 0.f;
-            u4[i] = 0.f;
+          for (int c = 0; c < 4; ++c) {
+            s4[c] = 0.f;
+            u4[c] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float d = __builtin_fmaf(z_at(i, j, r), kLog2e, nm2);
-              const float e = __builtin_amdgcn_exp2f(d);
-              s4[i] += e;
-              u4[i] = __builtin_fmaf(e, d, u4[i]);
+            for (int e = 0; e < 8; ++e) {
+              const float d = __builtin_fmaf(z_at(c + 4 * (e >> 2), j, e & 3), kLog2e, nm2);
+              const float ex = __builtin_amdgcn_exp2f(d);
+              s4[c] += ex;
+              u4[c] = __builtin_fmaf(ex, d, u4[c]);
             }
           }
           float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
           float u = (u4[0] + u4[1]) + (u4[2] + u4[3]);
+          s += __shfl_xor(s, 16);
+          u += __shfl_xor(u, 16);
           s += __shfl_xor(s, 32);
           u += __shfl_xor(u, 32);
           u *= kLn2;
@@ -771,7 +817,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           st_M[j] = mx;
           st_s[j] = s;
           st_u[j] = u;
-          if (wm == 1 && elane < 32) xch[col0 + j * 32] = make_float4(mx, s, u, 0.f);
+          if (wm == 1 && elane < 16) xch[col0 + j * 16] = make_float4(mx, s, u, 0.f);
         }
       };
       if (n_rows < kTile)
@@ -779,12 +825,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       else
         softmax_states(std::false_type{});
       __syncthreads();
-      if (wm == 0 && elane < 32) {
+      if (wm == 0 && elane < 16) {
         float4 *out = reinterpret_cast<float4 *>(a.part) + mi * a.T + t_tile;
         const int n_cols = (int)imin(a.T - t_tile, kTile);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = col0 + j * 32;
+        for (int j = 0; j < 8; ++j) {
+          const int col = col0 + j * 16;
           const float4 o = xch[col];
           float M = st_M[j], s = st_s[j], u = st_u[j];
           merge_state(M, s, u, o.x, o.y, o.z);
@@ -805,8 +851,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // kLsPitch-byte rows, and both layouts are then written with 16-byte stores.
       char *Ls = smem;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = col0 + j * 32;               // token within the pair tile
+      for (int j = 0; j < 8; ++j) {
+        const int col = col0 + j * 16;               // token within the pair tile
         const int64_t tile = wn ? pt1 : pt0;         // col / 128 == wn
         const int64_t t = tile * kSkipTile + (col & 127);
         const bool tok = tile >= 0 && t < a.T;
@@ -826,14 +872,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
         const int lim = act ? n_live : 0;  // columns >= lim are 0
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c0 = row0 + i * 32 + q * 8;  // first of 4 consecutive vocabulary rows
+        for (int i = 0; i < 8; ++i) {
+            const int c0 = row0 + i * 16;  // first of 4 consecutive vocabulary rows
             float d[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float z = acc[i][j][4 * q + c];
+              const float z = acc[i][j][c];
               const float p = __expf(z - lse_t);
               const float val = ga * ((c0 + c == yl ? 1.f : 0.f) - p) + gb * p * (ez - z);
               d[c] = (c0 + c < lim) ? val : 0.f;
@@ -880,31 +924,33 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       float *base = a.dh_acc + n_tile;  // + token * H
       if constexpr (kV2) {
         // fp32 sum over splits through LDS, half a tile at a time: in phase p every wave
-        // writes its row blocks i = 2p, 2p+1 as they sit in registers,
-        // [wave][i - 2p][j][r][lane] (constant offsets from one per-lane base); then wave
-        // w takes the 32 rows of block (wm, i) = (w / 2, 2p + w % 2) and adds the
-        // earlier splits' sum with 16-byte loads and stores (4 consecutive columns are
-        // 4 consecutive lanes of one register).
+        // writes its row blocks i = 4p .. 4p + 3 as they sit in registers,
+        // [wave][i - 4p][j][x][lane] with 64 bytes of padding after each (i, j) group
+        // (constant offsets from one per-lane base); then wave w takes the 32 rows of piece
+        // 4 (w / 2) + 2p + w % 2 (tile rows (w / 2) * 128 + 64 p + 32 (w % 2) ..) and adds
+        // the earlier splits' sum with 16-byte loads and stores (4 consecutive columns
+        // are 4 consecutive lanes of one register).  The skew puts the 16 lanes of a
+        // read on distinct banks.
         const int c4 = elane * 4;  // this lane's 4 columns in the row it handles
-        // column c4 sits in the registers of wave (wm, wn = c4 / 128), j = c4 / 32 % 4
-        const int lds_col = (c4 >> 7) * 32768 + ((c4 >> 5) & 3) * 4096 + (c4 & 31) * 4;
-        char *wb = smem + wave * 32768 + elane * 4;
+        // column c4 sits in the registers of wave (wm, wn = c4 / 128), j = c4 / 16 % 8,
+        // lanes c4 % 16 + 16 g4 ..
+        const int lds_col = (c4 >> 7) * kDhWave + ((c4 >> 4) & 7) * kDhGroup + (c4 & 15) * 4;
+        char *wb = smem + wave * kDhWave + elane * 4;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
-          for (int ii = 0; ii < 2; ++ii)
+          for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                *reinterpret_cast<float *>(wb + ((ii * 4 + j) * 16 + r) * 256) = acc[2 * p + ii][j][r];
+              for (int x = 0; x < 4; ++x)
+                *reinterpret_cast<float *>(wb + (ii * 8 + j) * kDhGroup + x * 256) = acc[4 * p + ii][j][x];
           __syncthreads();
-          const int rwm = wave >> 1, rii = wave & 1;  // the row block this wave stores
-          const int row_b = rwm * 128 + (2 * p + rii) * 32;
-          const int src_b = lds_col + rwm * 65536 + rii * 16384;  // + (g, r) of the row
-          // the block's 32 rows are one span piece: tokens pst .., valid below pln
+          const int rwm = wave >> 1, rh = wave & 1;  // the 32 rows this wave stores
+          const int src_b = lds_col + rwm * 2 * kDhWave;  // + the row's (ii, g4, x)
+          // the 32 rows are one span piece: tokens pst .., valid below pln
           int64_t pst, pln;
-          piece(a.span_tiles, 8 * mi + (row_b >> 5), uni(a.counts[2]), pst, pln);
+          piece(a.span_tiles, 8 * mi + 4 * rwm + 2 * p + rh, uni(a.counts[2]), pst, pln);
           const int n_in = (int)pln;
           float *bblk = base + pst * a.H;
 #pragma unroll
@@ -919,8 +965,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             }
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-              const int rr = k0 + kk;  // rr = 4 g + 8 (r / 4) + r % 4
-              const int src = src_b + (((rr >> 3) & 3) * 4 + (rr & 3)) * 256 + ((rr >> 2) & 1) * 128;
+              // row rr of the piece: block ii = 2 rh + rr / 16, g4 = rr % 16 / 4, x = rr % 4
+              const int rr = k0 + kk;
+              const int src = src_b + 64 * ((rr & 15) >> 2) + (2 * rh + (rr >> 4)) * 8 * kDhGroup + (rr & 3) * 256;
               if (rr < n_in && c4 < n_cols) {
                 float4 v = *reinterpret_cast<const float4 *>(smem + src);
                 v.x += prev[kk].x;
@@ -935,19 +982,19 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // tile rows wm * 128 + 32 i + .. are piece 4 wm + i
+        for (int i = 0; i < 8; ++i) {
+          // tile rows wm * 128 + 16 i + .. are rows 16 (i % 2) + .. of piece 4 wm + i / 2
           int64_t pst, pln;
-          piece(a.span_tiles, 8 * mi + 4 * wm + i, uni(a.counts[2]), pst, pln);
+          piece(a.span_tiles, 8 * mi + 4 * wm + (i >> 1), uni(a.counts[2]), pst, pln);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = (g << 2) + ((r >> 2) << 3) + (r & 3);
+          for (int x = 0; x < 4; ++x) {
+            const int lr = 16 * (i & 1) + 4 * (elane >> 4) + x;
             if (lr >= pln) continue;
             float *prow = base + (pst + lr) * a.H;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int col = col0 + j * 32;
-              if (col < n_cols) prow[col] = acc[i][j][r];
+            for (int j = 0; j < 8; ++j) {
+              const int col = col0 + j * 16;
+              if (col < n_cols) prow[col] = acc[i][j][x];
             }
           }
         }
@@ -960,29 +1007,26 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       T *base = reinterpret_cast<T *>(a.dW) + (a.v_base + v_tile) * a.H + n_tile;
       if constexpr (kV2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              ls_put4(col0 + j * 32, row0 + i * 32 + q * 8, acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          for (int i = 0; i < 8; ++i)
+            ls_put4(col0 + j * 16, row0 + i * 16, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         __syncthreads();
         ls_store_rows(reinterpret_cast<char *>(base), a.H, n_rows,
                       [&](int, int cb) -> int64_t { return cb < n_cols ? cb : -1; });
       } else {
         const uint32_t ldw = (uint32_t)a.H;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + i * 32 + ((r >> 2) << 3) + (r & 3);
+          for (int x = 0; x < 4; ++x) {
+            const int row = row0 + i * 16 + x;
             if (row >= n_rows) continue;
             T *prow = base + (uint32_t)row * ldw;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int col = col0 + j * 32;
-              if (col < n_cols) store1(prow + col, acc[i][j][r]);
+            for (int j = 0; j < 8; ++j) {
+              const int col = col0 + j * 16;
+              if (col < n_cols) store1(prow + col, acc[i][j][x]);
             }
           }
       }

@@ -177,11 +177,18 @@ def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols):
     """bf16 d-logits epilogue: the tile is staged token-major in LDS, then written
     token-major (16-byte chunks of 512-byte rows) and vocabulary-major (transposing
     LDS reads, 16-byte stores)."""
-    for j, i, q in itertools.product(range(4), range(4), range(4)):
-        col = (wave & 1) * 128 + (lane & 31) + j * 32
-        c0 = (wave >> 1) * 128 + (lane >> 5) * 4 + i * 32 + q * 8
+    for j, i in itertools.product(range(8), range(8)):
+        col = (wave & 1) * 128 + (lane & 15) + j * 16
+        c0 = (wave >> 1) * 128 + (lane >> 4) * 4 + i * 16
         a = col * LS_PITCH + c0 * 2
         assert (a >= 0).all() and (a + 8 <= LDS_DLG).all() and (a % 8 == 0).all()
+        # each half-wave of 8-byte writes covers the 64 banks once
+        for half in range(2):
+            sel = slice(32 * half, 32 * half + 32)
+            for w in range(4):
+                aw = a[w * 64:(w + 1) * 64][sel]
+                banks = {(int(x) // 4 + b) % 64 for x in aw for b in range(2)}
+                assert len(banks) == 64
     for k in range(32):
         tl = wave * 64 + 2 * k + (lane >> 5)
         cc = (lane & 31) * 8
@@ -229,8 +236,8 @@ def model(T, H, V, S_split, esz, mask, sample=False):
         else:
             load_rows_v1(src, K, esz, what, sample)
 
-    row_q = (wave >> 1) * 128 + (lane >> 5) * 4  # + i*32 + 8*(r//4) + r%4
-    col_q = (wave & 1) * 128 + (lane & 31)        # + j*32
+    row_q = (wave >> 1) * 128 + (lane >> 4) * 4  # + i*16 + x
+    col_q = (wave & 1) * 128 + (lane & 15)        # + j*16
 
     # ---- forward ----
     ldb = H * esz
@@ -277,13 +284,13 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                 if v2:
                     dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols)
                     continue
-                for j in range(4):
-                    col = col_q + j * 32
+                for j in range(8):
+                    col = col_q + j * 16
                     tl = np.array([pair[x] for x in col >> 7])
                     t = tl * SKIP + (col & 127)
                     tok, tokp = (tl >= 0) & (t < T), (tl >= 0) & (t < t_pad)
-                    for i, q in itertools.product(range(4), range(4)):
-                        c0 = row_q + i * 32 + q * 8
+                    for i in range(8):
+                        c0 = row_q + i * 16
                         ok = tok & (c0 < n_cols)
                         D.check((t[ok] * ld_d + v0 + c0[ok]) * esz, 4 * esz, "dlg store")
                         for c in range(4):
@@ -332,13 +339,13 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                     ok = (rr < np.array([pn[x] for x in sg])) & (c4 < min(H - n0, TILE))
                     acc.check((tok[ok] * H + n0 + c4[ok]) * 4, 16, "dh rmw")
                 continue
-            for i, r in itertools.product(range(4), range(16)):
-                row = row_q + i * 32 + ((r >> 2) << 3) + (r & 3)
+            for i, x in itertools.product(range(8), range(4)):
+                row = row_q + i * 16 + x
                 sg, lr = row >> 5, row & 31
                 t = np.array([ps[x] for x in sg]) + lr
                 okr = lr < np.array([pn[x] for x in sg])
-                for j in range(4):
-                    n = n0 + col_q + j * 32
+                for j in range(8):
+                    n = n0 + col_q + j * 16
                     ok = okr & (n < H)
                     acc.check((t[ok] * H + n[ok]) * 4, 4, "dh store")
         # ---- dWeight: A = vocabulary-major staging rows, B = h^T rows ----
@@ -356,10 +363,10 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                     ok = (m < min(Ws - v0, TILE)) & (cb < min(H - n0, TILE))
                     dW.check(((v_base + v0 + m[ok]) * H + n0 + cb[ok]) * esz, 16, "dw store (LDS)")
                 continue
-            for i, r in itertools.product(range(4), range(16)):
-                v = v0 + row_q + i * 32 + ((r >> 2) << 3) + (r & 3)
-                for j in range(4):
-                    n = n0 + col_q + j * 32
+            for i, x in itertools.product(range(8), range(4)):
+                v = v0 + row_q + i * 16 + x
+                for j in range(8):
+                    n = n0 + col_q + j * 16
                     ok = (v < Ws) & (n < H)
                     dW.check(((v_base + v[ok]) * H + n[ok]) * esz, esz, "dw store")
 
@@ -372,11 +379,11 @@ def model(T, H, V, S_split, esz, mask, sample=False):
             phys = l & 7
             assert (8 * w + k) * 1024 + l * 16 == row * 128 + phys * 16
             assert (8 * w + k) * 1024 + l * 16 + 16 <= OPSTAGE
-        for q, i, wb in itertools.product(range(4), range(4), (0, 128)):
+        for q, i, wb in itertools.product(range(2), range(8), (0, 128)):
             addrs = []
             for l in range(64):
-                R = wb + 32 * i + (l & 31)
-                a = R * 128 + ((((2 * q + (l >> 5)) ^ ((R >> 1) & 7))) << 4)
+                R = wb + 16 * i + (l & 15)
+                a = R * 128 + ((((4 * q + (l >> 4)) ^ ((R >> 1) & 7))) << 4)
                 assert a + 16 <= OPSTAGE
                 addrs.append(a)
             for quarter in range(4):
@@ -461,23 +468,33 @@ def test_tile_schedule_is_a_bijection(m_tiles, n_tiles, G):
 
 def test_dhidden_staging_map():
     """bf16 hidden-gradient epilogue: the LDS offsets each wave writes its accumulators
-    to and the offsets the storing waves read back name the same (row, column)."""
+    to and the offsets the storing waves read back name the same (row, column); the
+    16 lanes of each 16-byte read fall on distinct banks."""
+    DH_GROUP = 4 * 256 + 64
+    DH_WAVE = 32 * DH_GROUP
     written = {}
-    for w, l, p, ii, j, r in itertools.product(range(4), range(64), range(2), range(2), range(4), range(16)):
-        wm, wn, i = w >> 1, w & 1, 2 * p + ii
-        row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3)
-        col = wn * 128 + j * 32 + (l & 31)
-        off = w * 32768 + ((ii * 4 + j) * 16 + r) * 256 + l * 4
-        assert 0 <= off and off + 4 <= 131072 and (p, off) not in written
+    for w, l, p, ii, j, x in itertools.product(range(4), range(64), range(2), range(4), range(8), range(4)):
+        wm, wn, i = w >> 1, w & 1, 4 * p + ii
+        row = wm * 128 + i * 16 + 4 * (l >> 4) + x
+        col = wn * 128 + j * 16 + (l & 15)
+        off = w * DH_WAVE + (ii * 8 + j) * DH_GROUP + x * 256 + l * 4
+        assert w * DH_WAVE <= off and off + 4 <= (w + 1) * DH_WAVE <= 4 * DH_WAVE <= 160 * 1024
+        assert (p, off) not in written
         written[(p, off)] = (row, col)
-    for p, w, l, rr in itertools.product(range(2), range(4), range(64), range(32)):
-        c4 = l * 4
-        lds_col = (c4 >> 7) * 32768 + ((c4 >> 5) & 3) * 4096 + (c4 & 31) * 4
-        rwm, rii = w >> 1, w & 1
-        src = lds_col + rwm * 65536 + rii * 16384 + (((rr >> 3) & 3) * 4 + (rr & 3)) * 256 + ((rr >> 2) & 1) * 128
-        assert src % 16 == 0
-        for e in range(4):
-            assert written[(p, src + 4 * e)] == (rwm * 128 + (2 * p + rii) * 32 + rr, c4 + e)
+    for p, w, rr in itertools.product(range(2), range(4), range(32)):
+        rwm, rh = w >> 1, w & 1
+        srcs = []
+        for l in range(64):
+            c4 = l * 4
+            lds_col = (c4 >> 7) * DH_WAVE + ((c4 >> 4) & 7) * DH_GROUP + (c4 & 15) * 4
+            src = lds_col + rwm * 2 * DH_WAVE + 64 * ((rr & 15) >> 2) + (2 * rh + (rr >> 4)) * 8 * DH_GROUP + (rr & 3) * 256
+            assert src % 16 == 0
+            for e in range(4):
+                assert written[(p, src + 4 * e)] == (rwm * 128 + 64 * p + 32 * rh + rr, c4 + e)
+            srcs.append(src)
+        for quarter in range(4):
+            banks = {(srcs[x] // 4 + b) % 64 for x in range(16 * quarter, 16 * quarter + 16) for b in range(4)}
+            assert len(banks) == 64
 
 
 @pytest.mark.parametrize("seed", range(6))
