@@ -310,10 +310,14 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
     // live width of this split: the staging row stride and every grid below
     // come from it, never from S.
     const int64_t Ws = (V - sp * S) < S ? (V - sp * S) : S;
+    const int64_t ld_prev = a.ld_d;
     a.v_base = sp * S;
     a.Ws = (int32_t)Ws;
     a.ld_d = (int32_t)pad_ld(Ws);
     a.first_split = sp == 0;
+    // inactive token tiles: zero staging once per layout (the first split is the widest)
+    a.zero_vm = sp == 0;
+    a.zero_tm = sp == 0 || a.ld_d != ld_prev;
     a.Wt = base + L.Wt + (size_t)sp * (size_t)H * (size_t)L.ld_wt * (size_t)elt_size(dt);
     const int32_t tag = (int32_t)sp;
     const int64_t v_tiles = cdiv(Ws, kTile);

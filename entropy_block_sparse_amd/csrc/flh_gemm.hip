@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   } else if constexpr (KIND == kDlogits) {
     m_tiles = cdiv(a.Ws, kTile);
     n_pairs_gemm = cdiv(uni(a.counts[0]), 2);
-    n_pairs_all = cdiv(a.n_skip_tiles, 2);
+    n_pairs_all = (a.zero_tm || a.zero_vm) ? cdiv(a.n_skip_tiles, 2) : n_pairs_gemm;
     n_tiles = n_pairs_gemm;
     K = a.H;
   } else if constexpr (KIND == kDhidden) {
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         // token-major staging: rows of the pair's tokens, columns [c0, c1)
         constexpr int kChunks = kTile / kPer;
         char *Dw = const_cast<char *>(Dp);
-        for (int idx = tid; idx < kTile * kChunks; idx += kThreads) {
+        for (int idx = tid; a.zero_tm && idx < kTile * kChunks; idx += kThreads) {
           const int row = idx / kChunks;
           const int ch = idx - row * kChunks;
           const int64_t e = 2 * p + (row >> 7);
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t v1 = imin(c0 + kTile, (int64_t)a.Ws);
         constexpr int kVecTile = kSkipTile / kPer;  // 16-byte vectors per token tile
         char *Dtw = reinterpret_cast<char *>(a.Dt);
-        for (int idx = tid; idx < kTile * 2 * kVecTile; idx += kThreads) {
+        for (int idx = tid; a.zero_vm && idx < kTile * 2 * kVecTile; idx += kThreads) {
           const int vr = idx / (2 * kVecTile);
           const int rem = idx - vr * 2 * kVecTile;
           const int half = rem / kVecTile, vec = rem - half * kVecTile;

@@ -58,6 +58,11 @@ struct GemmArgs {
                            // rounded up to 16 bytes are written (zeros past T)
   float *dh_acc;           // fp32 hidden-gradient accumulator [T][H]
   int32_t first_split;     // dH: 1 -> overwrite, 0 -> accumulate
+  // d-logits: which staging layouts the token-tile pairs with no active token are
+  // zero-filled in.  Their d-logits are zero in every split, so the vocabulary-major
+  // layout (row stride fixed by T) needs it in the first split only; the token-major
+  // layout again whenever its row stride (from the split's live width) changes.
+  int32_t zero_tm, zero_vm;
   int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
                            // in flight on one XCD form a group_m x 32/group_m block)
   void *dW;                // [V][H]
