@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-trace", action="store_true")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="run one device copy of this many MiB first (counter calibration)")
+    p.add_argument("--skip-dw", action="store_true",
+                   help="weight gradient over active token tiles only (FLH_BWD_SKIP_INACTIVE_DW; "
+                        "the default keeps it dense)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the headline run: backward time of the stress workload at its "
                         "active fractions, fitted against the active-tile fraction")
@@ -94,7 +97,8 @@ def sweep(args):
             meta = None if dense else flh_spans_build(mask)
             lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
             ev[1].record()
-            flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b)
+            flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
+                         skip_inactive_dw=args.skip_dw)
             ev[2].record()
             torch.cuda.synchronize()
             if it >= args.warmup:
@@ -117,7 +121,8 @@ def sweep(args):
     out = {"metric": "stress-workload backward time vs active-tile fraction", "unit": "ms",
            "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "dtype": cfg.dtype, "data": "synthetic",
-           "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit},
+           "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
+                      "skip_inactive_dw": bool(args.skip_dw)},
            "points": points,
            "fit": {"model": "t_bwd = alpha + beta * (T_at + T_sp) / T", "alpha_ms": float(alpha),
                    "beta_ms": float(beta), "r2": r2}}
@@ -195,7 +200,8 @@ def main():
     def step():
         meta = None if args.dense else flh_spans_build(mask)
         lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
-        dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b)
+        dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
+                              skip_inactive_dw=args.skip_dw)
         return dH, dW
 
     if args.copy_calib_mib > 0:
@@ -229,7 +235,8 @@ def main():
     T_at, T_sp, spans = method_work(flh_spans_build(mask), T)
     A = int(mask_np.sum())
     pass_flops = 2.0 * H * V
-    F_method = pass_flops * (T + T_at + T_sp + T) if not args.dense else pass_flops * 4 * T
+    T_dw = T_at if (args.skip_dw and not args.dense) else T  # tokens the weight gradient covers
+    F_method = pass_flops * (T + T_at + T_sp + T_dw) if not args.dense else pass_flops * 4 * T
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32_MATRIX
 
     per_kernel = {}
@@ -244,7 +251,7 @@ def main():
     n_splits = -(-V // Ssplit)
     alg = {
         "fwd_logits_softmax": pass_flops * T,
-        "dweight": pass_flops * T / n_splits,
+        "dweight": pass_flops * T_dw / n_splits,
         "dlogits": pass_flops * T_at / n_splits,
         "dhidden_spans": pass_flops * T_sp / n_splits,
     }
@@ -278,7 +285,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
                    "active_frac": minfo["active_frac"], "mask_seed": minfo["seed"],
-                   "dense_fallback": bool(args.dense)},
+                   "dense_fallback": bool(args.dense), "skip_inactive_dw": bool(args.skip_dw)},
         "pct_peak_method": F_method / (ms * 1e-3) / peak,
         "work": {"A": A, "T_at128": int(T_at), "T_sp": int(T_sp), "spans": len(spans),
                  "F_method_tflop": F_method / 1e12, "F_dense_tflop": 4 * pass_flops * T / 1e12},

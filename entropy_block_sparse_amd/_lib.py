@@ -19,6 +19,7 @@ STATUS_NAMES = {
 }
 FLH_F32, FLH_BF16 = 0, 1
 OP_SPANS, OP_FORWARD, OP_BACKWARD = 0, 1, 2
+FLH_BWD_SKIP_INACTIVE_DW = 1  # flh_backward_ex option (include/flh.h)
 
 
 class FlhError(RuntimeError):
@@ -60,6 +61,9 @@ SIGNATURES = [
     ("flh_backward", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
       _I64, _I64, _I64, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    ("flh_backward_ex", ctypes.c_int,
+     [ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
+      _I64, _I64, _I64, _I32, _VP, _VP, _VP, _SZ, _VP, ctypes.c_uint32]),
     ("flh_trace_begin", ctypes.c_int, [_I32]),
     ("flh_trace_end", _I32, [ctypes.POINTER(TraceRecord), _I32]),
     ("flh_kernel_name", ctypes.c_char_p, [_I32]),

@@ -80,7 +80,7 @@ BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   const int64_t w_max = V < S ? V : S;
   const int64_t ld_max = pad_ld(w_max);
   L.ld_wt = pad_ld(w_max);
-  L.ld_t = pad_ld(T);
+  L.ld_t = pad_ld(cdiv(T, kSkipTile) * kSkipTile);  // room for whole 128-token tiles
   const size_t esz = (size_t)elt_size(dt);
   size_t off = 0;
   L.counts = off;
@@ -243,7 +243,18 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
                         const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
                         int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
                         size_t ws_bytes, void *stream) {
+  return flh_backward_ex(dt, h, W, targets, lse, entropy, grad_logprob, grad_entropy, loss_mask, meta, T,
+                         H, V, vocab_split, d_hidden, d_weight, ws, ws_bytes, stream, 0u);
+}
+
+flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                           const float *lse, const float *entropy, const float *grad_logprob,
+                           const float *grad_entropy, const uint8_t *loss_mask,
+                           const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
+                           int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
+                           size_t ws_bytes, void *stream, uint32_t flags) {
   if (!dtype_ok(dt)) return FLH_E_DTYPE;
+  if (flags & ~(uint32_t)FLH_BWD_SKIP_INACTIVE_DW) return FLH_E_UNSUPPORTED;
   if (!h || !W || !targets || !lse || !entropy || !d_hidden || !d_weight || !ws) return FLH_E_NULL;
   const int32_t S = split_or_default(vocab_split);
   if (!dims_ok(dt, T, H, V) || S <= 0 || S % kTile != 0) return FLH_E_SHAPE;
@@ -286,6 +297,8 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
   a.ld_t = L.ld_t;
   a.dh_acc = reinterpret_cast<float *>(base + L.acc);
   a.dW = d_weight;
+  // without metadata every tile is active and the compact layout is the dense one
+  a.compact_dw = (flags & FLH_BWD_SKIP_INACTIVE_DW) && meta ? 1 : 0;
 
   flh_status s = run(kIdBwdLists, -1, st, [&] {
     return launch_lists(T, meta ? meta->tile_bits : nullptr, meta ? meta->spans : nullptr,
@@ -300,6 +313,8 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
   });
   if (s != FLH_OK) return s;
   s = run(kIdTranspose, -1, st, [&] {
+    if (a.compact_dw)  // h^T over the active token tiles only, in tile-list order
+      return launch_transpose((int)elt_size(dt), h, T, H, base + L.ht, L.ld_t, 0, st, a.tile_list, a.counts);
     return launch_transpose((int)elt_size(dt), h, T, H, base + L.ht, L.ld_t, 0, st);
   });
   if (s != FLH_OK) return s;
@@ -316,7 +331,7 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
     a.ld_d = (int32_t)pad_ld(Ws);
     a.first_split = sp == 0;
     // inactive token tiles: zero staging once per layout (the first split is the widest)
-    a.zero_vm = sp == 0;
+    a.zero_vm = sp == 0 && !a.compact_dw;
     a.zero_tm = sp == 0 || a.ld_d != ld_prev;
     a.Wt = base + L.Wt + (size_t)sp * (size_t)H * (size_t)L.ld_wt * (size_t)elt_size(dt);
     const int32_t tag = (int32_t)sp;

@@ -399,6 +399,9 @@ hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, co
 // walking the tile grid with a stride of the launch size.  The backward uses it to
 // lay W (one block per vocabulary split) and h out with the contraction index
 // contiguous for the hidden- and weight-gradient products.
+// Gather form (row_tiles set, one block): output column r takes input row
+// row_tiles[r / 128] * 128 + r % 128 for r < 128 * n_row_tiles[0] (zero past R); the
+// columns past that are not written.
 namespace flh {
 namespace {
 
@@ -407,24 +410,34 @@ constexpr int kTrTile = 64;
 template <typename E>
 __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, int64_t R, int64_t C,
                                                         E *__restrict__ out, int64_t ld_out, int64_t block,
-                                                        int64_t c_tiles, int64_t r_tiles, int64_t n_tiles) {
+                                                        int64_t c_tiles, int64_t r_tiles, int64_t n_tiles,
+                                                        const int32_t *__restrict__ row_tiles,
+                                                        const int32_t *__restrict__ n_row_tiles) {
   constexpr int kT = kTrTile;
   constexpr int kV = 16 / sizeof(E);  // elements per 16-byte vector
   constexpr int kVecRow = kT / kV;    // vectors per tile row
   __shared__ E tile[kT][kT + kV];     // padded rows
   const int tid = threadIdx.x;
+  const bool gather = row_tiles != nullptr;
+  const int64_t R_gather = gather ? (int64_t)n_row_tiles[0] * 128 : 0;
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     // tile (blk, rt, ct): rows blk * block + rt * 64 .., columns ct * 64 ..
     const int64_t blk = t / (r_tiles * c_tiles);
     const int64_t rem = t - blk * r_tiles * c_tiles;
     const int64_t rb = (rem / c_tiles) * kT, c0 = (rem % c_tiles) * kT;  // block-local row
     const int64_t r0 = blk * block + rb;                                   // row of `in`
-    const int64_t R_blk = (R - blk * block) < block ? (R - blk * block) : block;
+    const int64_t R_blk = gather ? R_gather : ((R - blk * block) < block ? (R - blk * block) : block);
+    if (gather && rb >= R_blk) continue;  // past the gathered rows: not written (whole workgroup)
     E *outb = out + blk * C * ld_out;
     for (int idx = tid; idx < kT * kVecRow; idx += 256) {
       const int rr = idx / kVecRow, cv = (idx % kVecRow) * kV;
-      const int64_t r = r0 + rr, c = c0 + cv;
-      const bool live = rb + rr < R_blk;  // a row of this block (rows past it read as 0)
+      const int64_t c = c0 + cv;
+      int64_t r = r0 + rr;
+      bool live = rb + rr < R_blk;  // a row of this block (rows past it read as 0)
+      if (gather && live) {
+        r = (int64_t)row_tiles[(rb + rr) >> 7] * 128 + ((rb + rr) & 127);
+        live = r < R;
+      }
       E v[kV];
       if (live && c + kV <= C) {
         const uint4 x = *reinterpret_cast<const uint4 *>(in + r * C + c);
@@ -459,8 +472,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
 }  // namespace
 
 hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
-                            int64_t block, hipStream_t st) {
+                            int64_t block, hipStream_t st, const int32_t *row_tiles,
+                            const int32_t *n_row_tiles) {
   if (block <= 0) block = R;
+  if (row_tiles && (block != R || !n_row_tiles)) return hipErrorInvalidValue;
   if (block % kTrTile != 0 && block != R) return hipErrorInvalidValue;
   const int64_t c_tiles = (C + kTrTile - 1) / kTrTile;
   const int64_t r_tiles = (ld_out + kTrTile - 1) / kTrTile;  // per block
@@ -471,11 +486,11 @@ hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void 
   if (esz == 2)
     hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t *>(in), R, C, reinterpret_cast<uint16_t *>(out),
-                       ld_out, block, c_tiles, r_tiles, n_tiles);
+                       ld_out, block, c_tiles, r_tiles, n_tiles, row_tiles, n_row_tiles);
   else
     hipLaunchKernelGGL(transpose_kernel<float>, dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const float *>(in), R, C, reinterpret_cast<float *>(out), ld_out,
-                       block, c_tiles, r_tiles, n_tiles);
+                       block, c_tiles, r_tiles, n_tiles, row_tiles, n_row_tiles);
   return hipGetLastError();
 }
 

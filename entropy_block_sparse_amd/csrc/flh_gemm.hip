@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   } else {
     m_tiles = cdiv(a.Ws, kTile);
     n_tiles = cdiv(a.H, kTile);
-    K = a.T;
+    K = a.compact_dw ? (int64_t)uni(a.counts[0]) * kSkipTile : a.T;
   }
   const int64_t n_gemm = m_tiles * n_tiles;
   const int64_t n_items =
@@ -330,6 +330,21 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
     int64_t mi, ni;
     group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : 8, mi, ni);
+
+    if constexpr (KIND == kDweight) {
+      if (K == 0) {  // weight gradient over no active token tile (compact form): zeros
+        const int64_t v_tile = mi * kTile, n_tile = ni * kTile;
+        const int n_rows = (int)imin(a.Ws - v_tile, kTile), n_cols = (int)imin(a.H - n_tile, kTile);
+        char *zb = reinterpret_cast<char *>(a.dW) + ((a.v_base + v_tile) * a.H + n_tile) * kEsz;
+        constexpr int kCh = kTile / kPer;  // 16-byte chunks per tile row
+        for (int idx = tid; idx < kTile * kCh; idx += kThreads) {
+          const int r = idx / kCh, c = (idx - r * kCh) * kPer;
+          if (r < n_rows && c < n_cols)
+            *reinterpret_cast<u32x4 *>(zb + ((int64_t)r * a.H + c) * kEsz) = u32x4{0u, 0u, 0u, 0u};
+        }
+        continue;
+      }
+    }
 
     // ---------------- operand rows ----------------
     RowSrc srcA, srcB;
@@ -843,6 +858,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int n_cols = (int)imin(cdiv(a.Ws, kPer) * kPer - v_tile, kTile);  // written columns
       const int64_t t_pad = cdiv(a.T, kPer) * kPer;  // tokens written, zero padding included
       // the pair's two token tiles (the second may be missing)
+      const int64_t n_act = uni(a.counts[0]);  // active token tiles
       const int64_t pt0 = uni(a.tile_list[2 * ni]);
       const int64_t pt1 = (2 * ni + 1 < a.n_skip_tiles) ? uni(a.tile_list[2 * ni + 1]) : -1;
       T *Dd = reinterpret_cast<T *>(a.D) + v_tile;
@@ -886,10 +902,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
               ls_put4(col, c0, d[0], d[1], d[2], d[3]);
             } else {
               if (tok && c0 < n_cols) store4(Dd + t * a.ld_d + c0, d[0], d[1], d[2], d[3]);
-              if (tile >= 0 && t < t_pad) {  // a token or its zero padding
+              // vocabulary-major column: the token, or its slot among the active tiles
+              const int64_t rank = 2 * ni + (col >> 7);
+              const int64_t tc = a.compact_dw ? rank * kSkipTile + (col & 127) : t;
+              if (tile >= 0 && (a.compact_dw ? rank < n_act : t < t_pad)) {  // a token or padding
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (c0 + c < n_live) store1(Dv + (int64_t)(c0 + c) * a.ld_t + t, d[c]);
+                  if (c0 + c < n_live) store1(Dv + (int64_t)(c0 + c) * a.ld_t + tc, d[c]);
               }
             }
           }
@@ -912,10 +931,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
         // vocabulary-major: rows v of the split, tokens of the pair (zero padding to a
         // whole 16-byte chunk included)
+        // first column of each of the pair's tiles: its first token, or (compact) its
+        // slot among the active tiles; -1: not stored
+        const bool cpt = a.compact_dw != 0;
+        const int64_t vcol0 = uni(pt0 < 0 ? -1 : (cpt ? (2 * ni < n_act ? 2 * ni * kSkipTile : -1) : pt0 * kSkipTile));
+        const int64_t vcol1 =
+            uni(pt1 < 0 ? -1 : (cpt ? (2 * ni + 1 < n_act ? (2 * ni + 1) * kSkipTile : -1) : pt1 * kSkipTile));
+        const int64_t vlim = uni(cpt ? a.ld_t : t_pad);
         ls_store_rows(Dvb, a.ld_t, n_live, [&](int k, int cb) -> int64_t {
-          const int64_t tile = (k >> 2) ? pt1 : pt0;  // cb / 128
-          const int64_t t = tile * kSkipTile + (cb & 127);
-          return (tile >= 0 && t < t_pad) ? t : -1;
+          const int64_t base = (k >> 2) ? vcol1 : vcol0;  // cb / 128
+          const int64_t c = base + (cb & 127);
+          return (base >= 0 && c < vlim) ? c : -1;
         });
       }
     } else if constexpr (KIND == kDhidden) {

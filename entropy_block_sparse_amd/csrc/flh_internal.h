@@ -63,6 +63,10 @@ struct GemmArgs {
   // layout (row stride fixed by T) needs it in the first split only; the token-major
   // layout again whenever its row stride (from the split's live width) changes.
   int32_t zero_tm, zero_vm;
+  // Weight gradient over active token tiles only: the vocabulary-major staging and
+  // h^T hold just the active 128-token tiles, in the order of the tile list (column
+  // 128 r + j is token j of the r-th active tile), and dW contracts over those.
+  int32_t compact_dw;
   int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
                            // in flight on one XCD form a group_m x 32/group_m block)
   void *dW;                // [V][H]
@@ -91,8 +95,12 @@ hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void
 // block b becomes its own [C][ld_out] matrix at out + b * C * ld_out:
 // out_b[c][r] = in[b * block + r][c] for rows of the block, and 0 for the rest of
 // [0, ld_out).
+// Gather form: row_tiles (device, 128-row tiles of `in`) and n_row_tiles (device
+// count) set, block = R: output column r = input row row_tiles[r / 128] * 128 + r % 128,
+// for r < 128 * n_row_tiles[0] only.
 hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
-                            int64_t block, hipStream_t st);
+                            int64_t block, hipStream_t st, const int32_t *row_tiles = nullptr,
+                            const int32_t *n_row_tiles = nullptr);
 
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc,
                            const uint8_t *mask, void *dh, hipStream_t st);

@@ -184,6 +184,32 @@ flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_
                         int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* Options of flh_backward_ex. */
+enum {
+  /* Weight gradient over the active token tiles only.  Rows of d-logits of tokens in
+   * a tile without an active token are zero, so leaving those tiles out of
+   * dW = D^T h changes no product: the result is the dense one (bitwise, since the
+   * remaining partial sums are formed in the same groups and order).  The
+   * vocabulary-major staging and h^T then hold only the active tiles, so no zeros
+   * are stored or read for the others.  This is the next step the analysis of the
+   * method lists after the dense weight gradient, which the pages keep dense on
+   * purpose (SkyRL #2376, "How it works": weight gradients stay a dense
+   * contraction).  Has no effect when meta is NULL (every tile is active). */
+  FLH_BWD_SKIP_INACTIVE_DW = 1u
+};
+
+/*
+ * flh_backward with options: `flags` is a bitwise OR of FLH_BWD_* values (0 gives
+ * flh_backward).  Arguments, workspace and errors as for flh_backward, and
+ * FLH_E_UNSUPPORTED for an unknown flag bit.
+ */
+flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                           const float *lse, const float *entropy, const float *grad_logprob,
+                           const float *grad_entropy, const uint8_t *loss_mask,
+                           const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
+                           int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
+                           size_t ws_bytes, void *stream, uint32_t flags);
+
 /*
  * Launch tracing (profiling aid).  Between flh_trace_begin and flh_trace_end on
  * the same host thread, every kernel launch of the calls above is bracketed by a

@@ -8,6 +8,8 @@ At full size the fp64 oracle cannot afford every output, so:
   against the oracle's per-token definitions, which are exact at any T because each
   token's outputs depend on its own hidden row alone (SkyRL #2376, "How it works");
 * every inactive d_hidden row: bitwise +0;
+* the weight gradient over active token tiles only (FLH_BWD_SKIP_INACTIVE_DW): d_hidden
+  and d_weight bitwise equal to the dense mode's;
 * d_weight, which depends on every token, through identities that hold at any size:
   each row of the d-logits sums to zero over the vocabulary (both the log-prob and the
   entropy terms do), so sum_v dW[v, :] = 0; and <dH, h> = <dW, W> = sum D * z.
@@ -119,7 +121,14 @@ def test_full_size_spot_checks(cid, frac):
     lhs = float((dH.double() * h.double()).sum())
     rhs = float((dW64 * W.double()).sum())
     assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs)), (lhs, rhs)
-    del dW64, dH, dW, h, W
+    del dW64
+
+    # the weight gradient over active token tiles only equals the dense one bitwise
+    dH2, dW2 = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                            m_dev, meta, cfg.vocab_split, skip_inactive_dw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dH, dH2) and torch.equal(dW, dW2)
+    del dH, dW, dH2, dW2, h, W
     torch.cuda.empty_cache()
 
 

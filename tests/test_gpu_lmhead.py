@@ -40,9 +40,10 @@ def bursty_mask(T, seed, p_on=0.5, max_run=400):
 
 
 def run_case(T, H, V, dtype, mask, mode="lp+ent", vocab_split=0, use_meta=True, seed=0,
-             check_rows=True):
+             check_rows=True, skip_dw=False):
     dev = cuda_device()
-    announce(f"lmhead T={T} H={H} V={V} {dtype} mode={mode} split={vocab_split} meta={use_meta}")
+    announce(f"lmhead T={T} H={H} V={V} {dtype} mode={mode} split={vocab_split} meta={use_meta} "
+             f"skip_dw={skip_dw}")
     h, W, y = make_tensors(T, H, V, dtype, seed, device="cpu")
     h, W, y = h.to(dev), W.to(dev), y.to(dev)
     a, b = make_upstream(mask, mode, seed=seed)
@@ -51,7 +52,8 @@ def run_case(T, H, V, dtype, mask, mode="lp+ent", vocab_split=0, use_meta=True, 
     g_ent = None if b is None else torch.as_tensor(b).to(dev)
     lp, ent, lse = flh_forward(h, W, y)
     meta = flh_spans_build(m_dev) if use_meta else None
-    dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, m_dev, meta, vocab_split)
+    dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, m_dev, meta, vocab_split,
+                          skip_inactive_dw=skip_dw)
     torch.cuda.synchronize()
 
     hh, WW, yy = host64(h), host64(W), y.cpu().numpy()
@@ -157,3 +159,49 @@ def test_workload_mask_slices():
     for cid, (T, H, V) in [(2, (3000, 256, 6000)), (3, (2048, 128, 3100)), (4, (4096, 64, 5000))]:
         mask, _ = make_mask(cid, T=T)
         run_case(T, H, V, "bf16", mask, vocab_split=2048, seed=100 + cid)
+
+
+SKIP_DW_CASES = [
+    # dtype, T, H, V, split, mask: ragged T (partial last tile), a K tail, three splits
+    # with a live-width tail; a single active token; all active; none active
+    ("bf16", 1000, 520, 5000, 2048, "bursty"),
+    ("f32", 1000, 520, 5000, 2048, "bursty"),
+    ("bf16", 900, 256, 4000, 1024, "single"),
+    ("bf16", 777, 128, 2600, 1024, "all"),
+    ("bf16", 300, 64, 900, 512, "none"),
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,V,split,kind", SKIP_DW_CASES)
+def test_skip_inactive_dw_matches_dense(dtype, T, H, V, split, kind):
+    """The weight gradient over active token tiles only (FLH_BWD_SKIP_INACTIVE_DW)
+    leaves out products with zero d-logits rows only, and forms the remaining partial
+    sums in the same groups and order: d_hidden and d_weight equal the dense mode's
+    bitwise, and the oracle within the usual tolerances."""
+    if kind == "bursty":
+        mask = bursty_mask(T, 21)
+    elif kind == "single":
+        mask = np.zeros(T, np.uint8)
+        mask[513] = 1
+    elif kind == "all":
+        mask = np.ones(T, np.uint8)
+    else:
+        mask = np.zeros(T, np.uint8)
+    if kind == "none":
+        dev = cuda_device()
+        announce(f"skip_dw: no active token T={T}")
+        h, W, y = [x.to(dev) for x in make_tensors(T, H, V, dtype, 22)]
+        m = torch.as_tensor(mask).to(dev)
+        lp, ent, lse = flh_forward(h, W, y)
+        meta = flh_spans_build(m)
+        g = torch.zeros(T, dtype=torch.float32, device=dev)
+        out = [flh_backward(h, W, y, lse, ent, g, g, m, meta, split, skip_inactive_dw=s) for s in (False, True)]
+        torch.cuda.synchronize()
+        assert float(out[1][1].float().abs().max()) == 0.0 and not out[1][0].view(torch.int16).any()
+        assert torch.equal(out[0][1], out[1][1])
+        return
+    r_dense = run_case(T, H, V, dtype, mask, vocab_split=split, seed=23, check_rows=kind != "single")
+    r_skip = run_case(T, H, V, dtype, mask, vocab_split=split, seed=23, check_rows=kind != "single",
+                      skip_dw=True)
+    assert torch.equal(r_dense["dH"], r_skip["dH"])
+    assert torch.equal(r_dense["dW"], r_skip["dW"])

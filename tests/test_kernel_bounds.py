@@ -133,24 +133,34 @@ def span_pieces(spans, piece=PIECE):
     return out
 
 
-def transpose_model(inp, R, C, out, ld_out, esz, what, block=0):
+def transpose_model(inp, R, C, out, ld_out, esz, what, block=0, tiles=None):
     """Blocked transpose over 64 x 64 tiles: block b of `block` rows of `in` becomes
     out_b = out + b * C * ld_out, [C][ld_out].  16-byte loads where the vector is whole,
-    element loads otherwise; stores likewise.  Checks bounds and that every output
-    element (block, c < C, r < ld_out) is written exactly once."""
+    element loads otherwise; stores likewise.  Gather form (`tiles`: the 128-row tiles
+    to take, one block): output column r is input row tiles[r // 128] * 128 + r % 128,
+    columns from 128 * len(tiles) on are not written.  Checks bounds and that every
+    output element (block, c < C, r < ld_out, or r < 128 * len(tiles)) is written
+    exactly once."""
     kV = 16 // esz
     block = block or R
     n_blocks = cdiv(R, block)
     written = np.zeros((n_blocks, C, ld_out), np.int32)
     for blk in range(n_blocks):
-        R_blk = min(block, R - blk * block)
+        R_blk = min(block, R - blk * block) if tiles is None else 128 * len(tiles)
+        assert tiles is None or 128 * len(tiles) <= ld_out
         for t0 in range(cdiv(ld_out, 64)):
+            if tiles is not None and t0 * 64 >= R_blk:
+                continue
             for c0t in range(cdiv(C, 64)):
                 rb, c0 = t0 * 64, c0t * 64
                 idx = np.arange(64 * (64 // kV))
                 rr, cv = idx // (64 // kV), (idx % (64 // kV)) * kV
                 r, c = blk * block + rb + rr, c0 + cv
                 live = rb + rr < R_blk
+                if tiles is not None:
+                    src = np.where(live, np.array([tiles[min(x, len(tiles) - 1)] for x in (rb + rr) >> 7]), 0)
+                    r = src * 128 + ((rb + rr) & 127)
+                    live = live & (r < R)
                 whole = live & (c + kV <= C)
                 inp.check((r[whole] * C + c[whole]) * esz, 16, what + " load")
                 for e in range(kV):
@@ -167,13 +177,16 @@ def transpose_model(inp, R, C, out, ld_out, esz, what, block=0):
                     ok = live & ~whole & (r + e < ld_out)
                     out.check((base + c[ok] * ld_out + r[ok] + e) * esz, esz, what + " store1")
                     written[blk, c[ok], r[ok] + e] += 1
-    assert (written == 1).all(), f"{what}: output not covered exactly once"
+    if tiles is None:
+        assert (written == 1).all(), f"{what}: output not covered exactly once"
+    else:
+        assert (written[:, :, :R_blk] == 1).all() and not written[:, :, R_blk:].any(), what
 
 
 LS_PITCH, LDS_DLG = 528, 256 * 528  # bf16 d-logits epilogue: LDS tile pitch and size
 
 
-def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols):
+def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols, ni=0, n_act=0, compact=False):
     """bf16 d-logits epilogue: the tile is staged token-major in LDS, then written
     token-major (16-byte chunks of 512-byte rows) and vocabulary-major (transposing
     LDS reads, 16-byte stores)."""
@@ -207,10 +220,14 @@ def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols):
         tile = pair[1] if k >> 2 else pair[0]
         t = tile * SKIP + (tb & 127)
         ok = (tile >= 0) & (t < t_pad) & (mb + li < n_live)
+        if compact:
+            rank = 2 * ni + (k >> 2)
+            t = rank * SKIP + (tb & 127)
+            ok = (tile >= 0) & (rank < n_act) & (mb + li < n_live)
         Dt.check(((v0 + mb[ok] + li[ok]) * ld_t + t[ok]) * 2, 16, "dlg store^T (LDS)")
 
 
-def model(T, H, V, S_split, esz, mask, sample=False):
+def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
     """Walks every (sampled) workgroup tile of the four contractions and checks loads
     (per the fp32 or bf16 load path) and epilogue stores against the buffers."""
     kper = 16 // esz
@@ -219,7 +236,7 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     W = Buf("W", V * H * esz)
     w_max = min(V, S_split)
     ld_max = pad_ld(w_max)
-    ld_wt, ld_t = pad_ld(w_max), pad_ld(T)
+    ld_wt, ld_t = pad_ld(w_max), pad_ld(cdiv(T, SKIP) * SKIP)
     t_pad = cdiv(T, kper) * kper  # tokens of the vocabulary-major staging that are written
     D = Buf("D", T * ld_max * esz)
     Dt = Buf("Dt", w_max * ld_t * esz)
@@ -251,11 +268,12 @@ def model(T, H, V, S_split, esz, mask, sample=False):
     # ---- backward: transposed copies, work lists ----
     if not sample:
         transpose_model(W, V, H, Wt, ld_wt, esz, "W^T", block=S_split)
-        transpose_model(h, T, H, ht, ld_t, esz, "h^T")
     flags = S.tile_flags(mask, SKIP)
     n_skip = len(flags)
     tile_list = [i for i, f in enumerate(flags) if f] + [i for i, f in enumerate(flags) if not f]
     n_act = sum(flags)
+    if not sample:
+        transpose_model(h, T, H, ht, ld_t, esz, "h^T", tiles=tile_list[:n_act] if compact else None)
     pieces = span_pieces(S.active_spans(mask, 128))
     dh_tiles = [pieces[PIECES_PER_TILE * m:PIECES_PER_TILE * (m + 1)]
                 for m in range(cdiv(len(pieces), PIECES_PER_TILE))]
@@ -282,7 +300,7 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                                 T - t1 * SKIP if t1 >= 0 else 0, ldb), H, "dlg B")
                 pair = (t0, t1)
                 if v2:
-                    dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols)
+                    dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols, ni, n_act, compact)
                     continue
                 for j in range(8):
                     col = col_q + j * 16
@@ -293,9 +311,12 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                         c0 = row_q + i * 16
                         ok = tok & (c0 < n_cols)
                         D.check((t[ok] * ld_d + v0 + c0[ok]) * esz, 4 * esz, "dlg store")
+                        rank = 2 * ni + (col >> 7)
+                        tc = rank * SKIP + (col & 127) if compact else t
+                        okc = (tl >= 0) & (rank < n_act) if compact else tokp
                         for c in range(4):
-                            ok = tokp & (c0 + c < n_live)
-                            Dt.check(((v0 + c0[ok] + c) * ld_t + t[ok]) * esz, esz, "dlg store^T")
+                            ok = okc & (c0 + c < n_live)
+                            Dt.check(((v0 + c0[ok] + c) * ld_t + tc[ok]) * esz, esz, "dlg store^T")
             for p in [x + n_pairs_gemm for x in _pick(n_pairs_all - n_pairs_gemm, sample)]:
                 c1 = min(v0 + TILE, w_pad)
                 chunks = TILE // kper
@@ -316,7 +337,8 @@ def model(T, H, V, S_split, esz, mask, sample=False):
                 tl = np.array([tile_list[x] if x < n_skip else -1 for x in e])
                 t = tl * SKIP + vec * kper
                 ok = (tl >= 0) & (v < min(v0 + TILE, Ws)) & (t < t_pad)
-                Dt.check((v[ok] * ld_t + t[ok]) * esz, 16, "dlg zero^T")
+                if not compact:  # (the compact layout holds no inactive tile)
+                    Dt.check((v[ok] * ld_t + t[ok]) * esz, 16, "dlg zero^T")
         # ---- dHidden over tiles of eight span pieces: A = staging rows, B = W^T rows ----
         ldd, ldw = ld_d * esz, ld_wt * esz
         for tp, ni in itertools.product([dh_tiles[x] for x in _pick(len(dh_tiles), sample)],
@@ -352,8 +374,16 @@ def model(T, H, V, S_split, esz, mask, sample=False):
         ldt = ld_t * esz
         for mi, ni in itertools.product(_pick(cdiv(Ws, TILE), sample), _pick(cdiv(H, TILE), sample)):
             v0, n0 = mi * TILE, ni * TILE
-            loads(Src.rows(Dt, v0 * ldt, Ws - v0, ldt), T, "dw A")
-            loads(Src.rows(ht, n0 * ldt, H - n0, ldt), T, "dw B")
+            K_dw = n_act * SKIP if compact else T
+            if K_dw > 0:
+                loads(Src.rows(Dt, v0 * ldt, Ws - v0, ldt), K_dw, "dw A")
+                loads(Src.rows(ht, n0 * ldt, H - n0, ldt), K_dw, "dw B")
+            else:  # nothing to contract: the tile is stored as zeros, 16 bytes per thread
+                idx = np.arange(TILE * (TILE // kper))
+                r, c = idx // (TILE // kper), (idx % (TILE // kper)) * kper
+                ok = (r < min(Ws - v0, TILE)) & (c < min(H - n0, TILE))
+                dW.check(((v_base + v0 + r[ok]) * H + n0 + c[ok]) * esz, 16, "dw zero tile")
+                continue
             if v2:
                 # LDS-staged rows, 16-byte stores (8 columns) via transposing reads
                 li, g4 = lane & 15, lane >> 4
@@ -405,6 +435,7 @@ def test_fp32_addressing_in_bounds(T, H, V, S_split):
     for mask in (np.ones(T, np.uint8), (rng.random(T) < 0.4).astype(np.uint8),
                  np.zeros(T, np.uint8)):
         model(T, H, V, S_split, esz, mask)
+        model(T, H, V, S_split, esz, mask, compact=True)
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
@@ -414,6 +445,8 @@ def test_kernel_addressing_full_workloads_sampled(cid):
     cfg = CONFIGS[cid]
     mask, _ = make_mask(cid, active_frac=0.5 if cid == 5 else None)
     model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2 if cfg.dtype == "bf16" else 4, mask, sample=True)
+    model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2 if cfg.dtype == "bf16" else 4, mask, sample=True,
+          compact=True)
 
 
 # ---- bf16 path: LDS-direct buffer loads ------------------------------------------------
@@ -427,6 +460,7 @@ def test_bf16_descriptors_in_bounds(T, H, V, S_split):
     rng = np.random.default_rng(T + 3 * V)
     for mask in (np.ones(T, np.uint8), (rng.random(T) < 0.4).astype(np.uint8), np.zeros(T, np.uint8)):
         model(T, H, V, S_split, 2, mask)
+        model(T, H, V, S_split, 2, mask, compact=True)
 
 
 # ---- tile schedule: XCD-aware remap and grouped rasterization ---------------------------
