@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--skip-dw", action="store_true",
                    help="weight gradient over active token tiles only (FLH_BWD_SKIP_INACTIVE_DW; "
                         "the default keeps it dense)")
+    p.add_argument("--skip-fwd", action="store_true",
+                   help="forward over active token tiles only (FLH_FWD_SKIP_INACTIVE; the default is "
+                        "the dense forward)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the headline run: backward time of the stress workload at its "
                         "active fractions, fitted against the active-tile fraction")
@@ -95,7 +98,8 @@ def sweep(args):
         for it in range(args.warmup + args.steps):
             ev[0].record()
             meta = None if dense else flh_spans_build(mask)
-            lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
+            lp, ent, lse = flh_forward(h, W, y, workspace=ws_f, meta=meta,
+                                       skip_inactive=args.skip_fwd and not dense)
             ev[1].record()
             flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
                          skip_inactive_dw=args.skip_dw)
@@ -122,7 +126,7 @@ def sweep(args):
            "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "dtype": cfg.dtype, "data": "synthetic",
            "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
-                      "skip_inactive_dw": bool(args.skip_dw)},
+                      "skip_inactive_dw": bool(args.skip_dw), "skip_inactive_fwd": bool(args.skip_fwd)},
            "points": points,
            "fit": {"model": "t_bwd = alpha + beta * (T_at + T_sp) / T", "alpha_ms": float(alpha),
                    "beta_ms": float(beta), "r2": r2}}
@@ -199,7 +203,8 @@ def main():
 
     def step():
         meta = None if args.dense else flh_spans_build(mask)
-        lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
+        lp, ent, lse = flh_forward(h, W, y, workspace=ws_f, meta=meta,
+                                   skip_inactive=args.skip_fwd and not args.dense)
         dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
                               skip_inactive_dw=args.skip_dw)
         return dH, dW
@@ -236,7 +241,8 @@ def main():
     A = int(mask_np.sum())
     pass_flops = 2.0 * H * V
     T_dw = T_at if (args.skip_dw and not args.dense) else T  # tokens the weight gradient covers
-    F_method = pass_flops * (T + T_at + T_sp + T_dw) if not args.dense else pass_flops * 4 * T
+    T_fwd = T_at if (args.skip_fwd and not args.dense) else T  # tokens the forward covers
+    F_method = pass_flops * (T_fwd + T_at + T_sp + T_dw) if not args.dense else pass_flops * 4 * T
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32_MATRIX
 
     per_kernel = {}
@@ -250,7 +256,7 @@ def main():
     # algorithmic flops per launch of each contraction kernel
     n_splits = -(-V // Ssplit)
     alg = {
-        "fwd_logits_softmax": pass_flops * T,
+        "fwd_logits_softmax": pass_flops * T_fwd,
         "dweight": pass_flops * T_dw / n_splits,
         "dlogits": pass_flops * T_at / n_splits,
         "dhidden_spans": pass_flops * T_sp / n_splits,
@@ -285,7 +291,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
                    "active_frac": minfo["active_frac"], "mask_seed": minfo["seed"],
-                   "dense_fallback": bool(args.dense), "skip_inactive_dw": bool(args.skip_dw)},
+                   "dense_fallback": bool(args.dense), "skip_inactive_dw": bool(args.skip_dw),
+                   "skip_inactive_fwd": bool(args.skip_fwd)},
         "pct_peak_method": F_method / (ms * 1e-3) / peak,
         "work": {"A": A, "T_at128": int(T_at), "T_sp": int(T_sp), "spans": len(spans),
                  "F_method_tflop": F_method / 1e12, "F_dense_tflop": 4 * pass_flops * T / 1e12},

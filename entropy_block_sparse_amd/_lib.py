@@ -20,6 +20,7 @@ STATUS_NAMES = {
 FLH_F32, FLH_BF16 = 0, 1
 OP_SPANS, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 FLH_BWD_SKIP_INACTIVE_DW = 1  # flh_backward_ex option (include/flh.h)
+FLH_FWD_SKIP_INACTIVE = 1  # flh_forward_ex option
 
 
 class FlhError(RuntimeError):
@@ -58,6 +59,9 @@ SIGNATURES = [
     ("flh_spans_build", ctypes.c_int, [_VP, ctypes.POINTER(ActiveMeta), _VP, _SZ, _VP]),
     ("flh_forward", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    ("flh_forward_ex", ctypes.c_int,
+     [ctypes.c_int, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta), _VP, _SZ,
+      _VP, ctypes.c_uint32]),
     ("flh_backward", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
       _I64, _I64, _I64, _I32, _VP, _VP, _VP, _SZ, _VP]),

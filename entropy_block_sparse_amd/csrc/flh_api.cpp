@@ -27,12 +27,13 @@ enum KernelId : int32_t {
   kIdDweight,
   kIdFinalize,
   kIdTranspose,
+  kIdFwdLists,
   kIdCount
 };
 const char *const kKernelNames[kIdCount] = {
     "spans_build", "fwd_logits_softmax", "fwd_combine", "bwd_lists",
     "dlogits",     "dhidden_spans",      "dweight",     "dhidden_finalize",
-    "transpose"};
+    "transpose",   "fwd_lists"};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -59,7 +60,14 @@ int64_t pad_ld(int64_t n) {
   return ld;
 }
 
-size_t fwd_bytes(int64_t T, int64_t V) { return (size_t)cdiv(V, kTile) * (size_t)T * 16; }
+// Forward workspace: per-tile softmax states [ceil(V/256)][T] float4, then (used by
+// the forward over active token tiles only) counts and the token-tile list.
+size_t fwd_part_bytes(int64_t T, int64_t V) { return (size_t)cdiv(V, kTile) * (size_t)T * 16; }
+size_t fwd_counts_off(int64_t T, int64_t V) { return align_up(fwd_part_bytes(T, V), 256); }
+size_t fwd_list_off(int64_t T, int64_t V) { return fwd_counts_off(T, V) + 256; }
+size_t fwd_bytes(int64_t T, int64_t V) {
+  return align_up(fwd_list_off(T, V) + (size_t)cdiv(T, kSkipTile) * sizeof(int32_t), 256);
+}
 
 struct BwdLayout {
   size_t counts, tile_list, span_tiles, D, Dt, Wt, ht, acc, total;
@@ -212,9 +220,23 @@ flh_status flh_spans_build(const uint8_t *loss_mask, flh_active_meta *meta, void
 flh_status flh_forward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
                        int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
                        void *ws, size_t ws_bytes, void *stream) {
+  return flh_forward_ex(dt, h, W, targets, T, H, V, logprob, entropy, lse, nullptr, ws, ws_bytes, stream, 0u);
+}
+
+flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                          int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
+                          const flh_active_meta *meta, void *ws, size_t ws_bytes, void *stream,
+                          uint32_t flags) {
   if (!dtype_ok(dt)) return FLH_E_DTYPE;
+  if (flags & ~(uint32_t)FLH_FWD_SKIP_INACTIVE) return FLH_E_UNSUPPORTED;
+  const bool skip = (flags & FLH_FWD_SKIP_INACTIVE) != 0;
   if (!h || !W || !targets || !logprob || !entropy || !lse || !ws) return FLH_E_NULL;
   if (!dims_ok(dt, T, H, V)) return FLH_E_SHAPE;
+  if (skip) {
+    if (!meta) return FLH_E_META;
+    if (!meta->tile_bits) return FLH_E_NULL;
+    if (meta->T != T || meta->tile_m != flh_tile_m(dt)) return FLH_E_META;
+  }
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(ws, 256)) return FLH_E_ALIGN;
   if (ws_bytes < fwd_bytes(T, V)) return FLH_E_WORKSPACE;
   const int cus = num_cus();
@@ -229,11 +251,28 @@ flh_status flh_forward(flh_dtype dt, const void *h, const void *W, const int64_t
   a.W = W;
   a.targets = targets;
   a.part = reinterpret_cast<float *>(ws);
-  const int grid = grid_for(cdiv(V, kTile) * cdiv(T, kTile), cus);
-  flh_status s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwd, a, grid, st); });
+  flh_status s = FLH_OK;
+  if (skip) {
+    // the active token tiles, ascending (the list builder without span pieces)
+    char *base = reinterpret_cast<char *>(ws);
+    a.counts = reinterpret_cast<int32_t *>(base + fwd_counts_off(T, V));
+    a.tile_list = reinterpret_cast<int32_t *>(base + fwd_list_off(T, V));
+    a.n_skip_tiles = (int32_t)cdiv(T, kSkipTile);
+    s = run(kIdFwdLists, -1, st, [&] {
+      return launch_lists(T, meta->tile_bits, nullptr, nullptr, 0, const_cast<int32_t *>(a.tile_list),
+                          const_cast<int32_t *>(a.counts), nullptr, 0, st);
+    });
+    if (s != FLH_OK) return s;
+    const int grid = grid_for(cdiv(V, kTile) * cdiv(a.n_skip_tiles, 2), cus);
+    s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwdSkip, a, grid, st); });
+  } else {
+    const int grid = grid_for(cdiv(V, kTile) * cdiv(T, kTile), cus);
+    s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwd, a, grid, st); });
+  }
   if (s != FLH_OK) return s;
   return run(kIdFwdCombine, -1, st, [&] {
-    return launch_combine((int)dt, T, H, V, h, W, a.part, targets, logprob, entropy, lse, st);
+    return launch_combine((int)dt, T, H, V, h, W, a.part, targets, logprob, entropy, lse, st,
+                          skip ? meta->tile_bits : nullptr);
   });
 }
 

@@ -228,13 +228,28 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
   }
 }
 
+// bits: NULL, or the tile bitmap of a forward over active 128-token tiles only; tokens
+// of the other tiles get 0 for all three outputs.
+__device__ __forceinline__ bool tile_skipped(const uint32_t *bits, int64_t t) {
+  if (!bits) return false;
+  const int64_t i = t / kSkipTile;
+  return ((bits[i >> 5] >> (i & 31)) & 1u) == 0;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int64_t V,
                                                       const float4 *__restrict__ part,
+                                                      const uint32_t *__restrict__ bits,
                                                       float *__restrict__ logprob,
                                                       float *__restrict__ entropy,
                                                       float *__restrict__ lse) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
+  if (tile_skipped(bits, t)) {
+    lse[t] = 0.f;
+    entropy[t] = 0.f;
+    logprob[t] = 0.f;
+    return;
+  }
   const float ninf = -__builtin_huge_valf();
   const int64_t n_vt = (V + kTile - 1) / kTile;
   float M = ninf, s = 0.f, u = 0.f;
@@ -265,11 +280,12 @@ __global__ __launch_bounds__(256) void target_logit_kernel(int64_t T, int64_t H,
                                                            const E *__restrict__ h,
                                                            const E *__restrict__ W,
                                                            const int64_t *__restrict__ targets,
+                                                           const uint32_t *__restrict__ bits,
                                                            float *__restrict__ out) {
   constexpr int kPer = 16 / sizeof(E);
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (t >= T) return;  // whole wavefronts
+  if (t >= T || tile_skipped(bits, t)) return;  // whole wavefronts
   const int64_t y = targets[t];
   if (y < 0 || y >= V) {
     if (lane == 0) out[t] = __builtin_nanf("");
@@ -355,21 +371,21 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
 
 hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
                           const float *part, const int64_t *targets, float *logprob, float *entropy,
-                          float *lse, hipStream_t st) {
+                          float *lse, hipStream_t st, const uint32_t *skip_bits) {
   const unsigned tl_blocks = (unsigned)((T + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(target_logit_kernel<uint16_t>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
                        reinterpret_cast<const uint16_t *>(h), reinterpret_cast<const uint16_t *>(W),
-                       targets, logprob);
+                       targets, skip_bits, logprob);
   else
     hipLaunchKernelGGL(target_logit_kernel<float>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
                        reinterpret_cast<const float *>(h), reinterpret_cast<const float *>(W), targets,
-                       logprob);
+                       skip_bits, logprob);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t blocks = (T + 255) / 256;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, T, V,
-                     reinterpret_cast<const float4 *>(part), logprob, entropy, lse);
+                     reinterpret_cast<const float4 *>(part), skip_bits, logprob, entropy, lse);
   return hipGetLastError();
 }
 

@@ -248,6 +248,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     m_tiles = cdiv(a.V, kTile);
     n_tiles = cdiv(a.T, kTile);
     K = a.H;
+  } else if constexpr (KIND == kFwdSkip) {
+    m_tiles = cdiv(a.V, kTile);
+    n_tiles = cdiv(uni(a.counts[0]), 2);  // pairs of active token tiles
+    K = a.H;
   } else if constexpr (KIND == kDlogits) {
     m_tiles = cdiv(a.Ws, kTile);
     n_pairs_gemm = cdiv(uni(a.counts[0]), 2);
@@ -352,6 +356,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int64_t v0 = mi * kTile, t0 = ni * kTile, ldb = a.H * kEsz;
       srcA = rows_of(Wp + v0 * ldb, a.V - v0, ldb);
       srcB = rows_of(hp + t0 * ldb, a.T - t0, ldb);
+    } else if constexpr (KIND == kFwdSkip) {
+      // the pair's tiles: active tiles 2 ni and 2 ni + 1 of the list (the second may not exist)
+      const int64_t v0 = mi * kTile, ldb = a.H * kEsz;
+      srcA = rows_of(Wp + v0 * ldb, a.V - v0, ldb);
+      const int64_t e1 = 2 * ni + 1;
+      const int64_t tile0 = uni(a.tile_list[2 * ni]);
+      const int64_t tile1 = (e1 < uni(a.counts[0])) ? uni(a.tile_list[e1]) : -1;
+      srcB = rows_of2(hp + tile0 * kSkipTile * ldb, a.T - tile0 * kSkipTile,
+                      hp + (tile1 >= 0 ? tile1 : tile0) * kSkipTile * ldb,
+                      tile1 >= 0 ? a.T - tile1 * kSkipTile : 0, ldb);
     } else if constexpr (KIND == kDlogits) {
       const int64_t v0 = mi * kTile, ldb = a.H * kEsz;
       const char *wb = Wp + (a.v_base + v0) * ldb;
@@ -574,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // The forward kernel gains nothing from it and is short of scalar registers, so
       // it runs without.
       constexpr int kPfAhead = 3;
-      constexpr bool kPrefetch = KIND != kFwd;
+      constexpr bool kPrefetch = KIND != kFwd && KIND != kFwdSkip;
       __amdgpu_buffer_rsrc_t rpf = rsrc(Wp, 0);
       uint32_t pf_vo = 0;
       if constexpr (kPrefetch) {
@@ -762,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
       }
     };
-    if constexpr (KIND == kFwd) {
+    if constexpr (KIND == kFwd || KIND == kFwdSkip) {
       // Per token (column) of the tile: max M of its logits over the tile's vocabulary
       // rows, s = sum e^(z - M), u = sum e^(z - M) (z - M).  Exponentials are taken in
       // base 2 (d = (z - M) log2 e, e = 2^d, u = ln 2 * sum e d); each sum runs as four
@@ -841,8 +855,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         softmax_states(std::false_type{});
       __syncthreads();
       if (wm == 0 && elane < 16) {
-        float4 *out = reinterpret_cast<float4 *>(a.part) + mi * a.T + t_tile;
-        const int n_cols = (int)imin(a.T - t_tile, kTile);
+        // tokens of the tile's columns: t_tile + col, or (pairs of active tiles) the
+        // first token of this wave's tile (columns wn * 128 ..) + col % 128
+        int64_t t_first = t_tile;
+        int n_cols = (int)imin(a.T - t_tile, kTile);
+        if constexpr (KIND == kFwdSkip) {
+          const int64_t tile = uni(2 * ni + wn < uni(a.counts[0]) ? a.tile_list[2 * ni + wn] : -1);
+          t_first = tile < 0 ? 0 : tile * kSkipTile - wn * 128;
+          n_cols = tile < 0 ? 0 : (int)imin(a.T - tile * kSkipTile + wn * 128, kTile);
+        }
+        float4 *out = reinterpret_cast<float4 *>(a.part) + mi * a.T + t_first;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int col = col0 + j * 16;
@@ -1074,6 +1096,7 @@ hipError_t launch_t(GemmKind kind, const GemmArgs &a, int grid, hipStream_t st) 
     case kDlogits: return launch_kind<T, kDlogits>(a, grid, st);
     case kDhidden: return launch_kind<T, kDhidden>(a, grid, st);
     case kDweight: return launch_kind<T, kDweight>(a, grid, st);
+    case kFwdSkip: return launch_kind<T, kFwdSkip>(a, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -23,6 +23,7 @@ enum GemmKind : int {
   kDlogits,   // recompute z over active token tiles -> d-logits  (K = H)
   kDhidden,   // dH[span rows] (+)= D[span rows, :] W_s           (K = W_s; B = W^T rows)
   kDweight,   // dW[split rows] = D^T h                          (K = T; A = D^T rows, B = h^T rows)
+  kFwdSkip,   // kFwd over pairs of active 128-token tiles only    (K = H)
 };
 
 // Everything a contraction kernel needs; plain data, passed by value.
@@ -86,9 +87,11 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
 
 // Target logits z_y = h[t] . W[y_t] into logprob, then the merge of the per-tile
 // softmax states into lse, entropy and logprob = z_y - lse.
+// skip_bits: NULL, or the tile bitmap of a forward over active token tiles only (the
+// other tiles' tokens get 0 for all three outputs).
 hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
                           const float *part, const int64_t *targets, float *logprob, float *entropy,
-                          float *lse, hipStream_t st);
+                          float *lse, hipStream_t st, const uint32_t *skip_bits = nullptr);
 
 // Blocked transpose: rows of `in` ([R][C] row-major, elements of esz bytes, 2 or 4)
 // are taken in blocks of `block` rows (a multiple of 64; 0 = one block of R rows);

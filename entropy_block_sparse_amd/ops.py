@@ -14,7 +14,8 @@ from typing import List, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import FLH_BF16, FLH_BWD_SKIP_INACTIVE_DW, FLH_F32, OP_BACKWARD, OP_FORWARD, ActiveMeta, check, lib
+from ._lib import (FLH_BF16, FLH_BWD_SKIP_INACTIVE_DW, FLH_F32, FLH_FWD_SKIP_INACTIVE, OP_BACKWARD, OP_FORWARD,
+                   ActiveMeta, check, lib)
 
 DEFAULT_MAX_GAP = 128
 DEFAULT_VOCAB_SPLIT = 16384
@@ -123,8 +124,12 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
 
 
 def flh_forward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
-                workspace: Optional[torch.Tensor] = None):
-    """Returns (logprob, entropy, lse), each float32 [T]."""
+                workspace: Optional[torch.Tensor] = None, meta: Optional["ActiveMetaTensors"] = None,
+                skip_inactive: bool = False):
+    """Returns (logprob, entropy, lse), each float32 [T].
+
+    skip_inactive: flh_forward_ex's FLH_FWD_SKIP_INACTIVE (needs meta): the forward over
+    active 128-token tiles only; the other tiles' tokens get 0."""
     _require_cuda(h, W, targets)
     if h.dtype != W.dtype:
         raise TypeError("h and W must share a dtype")
@@ -140,8 +145,15 @@ def flh_forward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     lse = torch.empty(T, dtype=torch.float32, device=dev)
     need = flh_workspace_bytes(OP_FORWARD, h.dtype, T, H, V)
     ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
-    check(lib().flh_forward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), T, H, V, _ptr(lp),
-                            _ptr(ent), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "flh_forward")
+    if skip_inactive:
+        if meta is None:
+            raise ValueError("skip_inactive needs the active metadata (flh_spans_build)")
+        check(lib().flh_forward_ex(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), T, H, V, _ptr(lp),
+                                   _ptr(ent), _ptr(lse), ctypes.byref(meta.struct), _ptr(ws), ws.numel(),
+                                   _stream(dev), FLH_FWD_SKIP_INACTIVE), "flh_forward_ex")
+    else:
+        check(lib().flh_forward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), T, H, V, _ptr(lp),
+                                _ptr(ent), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "flh_forward")
     return lp, ent, lse
 
 

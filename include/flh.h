@@ -121,7 +121,8 @@ int64_t flh_span_capacity(int64_t T, int32_t max_gap);
 /*
  * Workspace bytes the call `op` needs for these sizes (0 for FLH_OP_SPANS).
  * vocab_split 0 means 16384.  Returns 0 for invalid sizes as well.
- * Forward: per-tile softmax partials, ceil(V/256) * T * 16 bytes.
+ * Forward: per-tile softmax partials, ceil(V/256) * T * 16 bytes, and the active
+ * token-tile list (4 * ceil(T/128) bytes plus alignment).
  * Backward: work lists; the d-logits staging of the widest split in two layouts
  * (token-major T x W and vocabulary-major W x T, W = min(V, vocab_split)); W and h
  * transposed (H x V and H x T, so that every contraction reads its contraction
@@ -153,6 +154,28 @@ flh_status flh_spans_build(const uint8_t *loss_mask, flh_active_meta *meta, void
 flh_status flh_forward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
                        int64_t T, int64_t H, int64_t V, float *logprob, float *entropy,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* Options of flh_forward_ex. */
+enum {
+  /* Forward over the active 128-token tiles only (the block-sparse forward of the
+   * stack's previous layer, which the pages' baseline already includes; SkyRL #2376,
+   * "Performance" and the stack listed under "What does this PR do?").  Tokens of a
+   * tile without an active token get logprob = entropy = lse = 0; every other token's
+   * outputs equal the dense forward's bitwise.  Needs meta (from flh_spans_build on the
+   * loss mask), FLH_E_META without it or for a meta of another T or tile height. */
+  FLH_FWD_SKIP_INACTIVE = 1u
+};
+
+/*
+ * flh_forward with options: `flags` is a bitwise OR of FLH_FWD_* values (0 gives
+ * flh_forward; meta is then ignored and may be NULL).  Arguments, workspace and errors
+ * as for flh_forward, and FLH_E_UNSUPPORTED for an unknown flag bit.  A backward after
+ * it is exact: inactive tokens' saved values are never read.
+ */
+flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                          int64_t T, int64_t H, int64_t V, float *logprob, float *entropy,
+                          float *lse, const flh_active_meta *meta, void *ws, size_t ws_bytes,
+                          void *stream, uint32_t flags);
 
 /*
  * Backward: d_hidden [T,H] and d_weight [V,H] (dtype dt, both overwritten) from

@@ -56,8 +56,13 @@ def test_span_capacity_matches_oracle():
 def test_workspace_sizes():
     L = lib()
     f = L.flh_workspace_bytes
-    # forward: one 16-byte softmax state per (256-row vocabulary tile, token)
-    assert f(1, 1, 16384, 4096, 128256, 0) == ((128256 + 255) // 256) * 16384 * 16
+    # forward: one 16-byte softmax state per (256-row vocabulary tile, token), then
+    # 256 bytes of counts and the token-tile list (int32 per 128-token tile), each
+    # section 256-byte aligned
+    def up(x):
+        return (x + 255) // 256 * 256
+    parts = ((128256 + 255) // 256) * 16384 * 16
+    assert f(1, 1, 16384, 4096, 128256, 0) == up(up(parts) + 256 + 4 * (16384 // 128))
     b = f(2, 1, 16384, 4096, 128256, 0)
     assert b >= 16384 * 16384 * 2 + 16384 * 4096 * 4   # staging + fp32 accumulator
     assert f(2, 1, 512, 256, 4096, 0) < f(2, 1, 512, 256, 40960, 0)

@@ -8,6 +8,8 @@ At full size the fp64 oracle cannot afford every output, so:
   against the oracle's per-token definitions, which are exact at any T because each
   token's outputs depend on its own hidden row alone (SkyRL #2376, "How it works");
 * every inactive d_hidden row: bitwise +0;
+* the forward over active token tiles only (FLH_FWD_SKIP_INACTIVE): the dense outputs
+  bitwise on active tiles, zeros elsewhere;
 * the weight gradient over active token tiles only (FLH_BWD_SKIP_INACTIVE_DW): d_hidden
   and d_weight bitwise equal to the dense mode's;
 * d_weight, which depends on every token, through identities that hold at any size:
@@ -122,6 +124,16 @@ def test_full_size_spot_checks(cid, frac):
     rhs = float((dW64 * W.double()).sum())
     assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs)), (lhs, rhs)
     del dW64
+
+    # the forward over active token tiles only: the dense outputs on those tiles, 0 elsewhere
+    sp = flh_forward(h, W, y, meta=meta, skip_inactive=True)
+    torch.cuda.synchronize()
+    tiles = np.zeros(-(-T // 128), bool)
+    tiles[np.nonzero(mask)[0] // 128] = True
+    act_dev = torch.as_tensor(np.repeat(tiles, 128)[:T]).to(dev)
+    for d, s in zip((lp, ent, lse), sp):
+        assert torch.equal(d[act_dev], s[act_dev]) and not s[~act_dev].any()
+    del sp
 
     # the weight gradient over active token tiles only equals the dense one bitwise
     dH2, dW2 = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),

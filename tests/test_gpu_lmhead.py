@@ -205,3 +205,41 @@ def test_skip_inactive_dw_matches_dense(dtype, T, H, V, split, kind):
                       skip_dw=True)
     assert torch.equal(r_dense["dH"], r_skip["dH"])
     assert torch.equal(r_dense["dW"], r_skip["dW"])
+
+
+@pytest.mark.parametrize("dtype,T,H,V,split,kind", SKIP_DW_CASES)
+def test_forward_skip_inactive_matches_dense(dtype, T, H, V, split, kind):
+    """The forward over active 128-token tiles only (FLH_FWD_SKIP_INACTIVE): tokens of
+    active tiles get the dense forward's outputs bitwise (a token's outputs depend on
+    its own logits column only), the others exactly 0, and a backward from these outputs
+    equals the one from the dense forward bitwise."""
+    dev = cuda_device()
+    announce(f"forward skip T={T} H={H} V={V} {dtype} {kind}")
+    if kind == "bursty":
+        mask = bursty_mask(T, 31)
+    elif kind == "single":
+        mask = np.zeros(T, np.uint8)
+        mask[513] = 1
+    elif kind == "all":
+        mask = np.ones(T, np.uint8)
+    else:
+        mask = np.zeros(T, np.uint8)
+    h, W, y = [x.to(dev) for x in make_tensors(T, H, V, dtype, 32)]
+    m = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m)
+    dense = flh_forward(h, W, y)
+    sparse = flh_forward(h, W, y, meta=meta, skip_inactive=True)
+    torch.cuda.synchronize()
+    tiles = np.zeros(-(-T // 128), bool)
+    tiles[np.nonzero(mask)[0] // 128] = True
+    in_active = np.repeat(tiles, 128)[:T]
+    act_dev = torch.as_tensor(in_active).to(dev)
+    for d, s in zip(dense, sparse):
+        assert torch.equal(d[act_dev], s[act_dev])
+        assert not s[~act_dev].any()
+    a, b = make_upstream(mask)
+    g_lp, g_ent = torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev)
+    ref = flh_backward(h, W, y, dense[2], dense[1], g_lp, g_ent, m, meta, split)
+    out = flh_backward(h, W, y, sparse[2], sparse[1], g_lp, g_ent, m, meta, split)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], out[0]) and torch.equal(ref[1], out[1])

@@ -272,6 +272,20 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
     n_skip = len(flags)
     tile_list = [i for i, f in enumerate(flags) if f] + [i for i, f in enumerate(flags) if not f]
     n_act = sum(flags)
+    if compact:
+        # ---- forward over pairs of active token tiles only (same option run) ----
+        for mi, ni in itertools.product(_pick(cdiv(V, TILE), sample), _pick(cdiv(n_act, 2), sample)):
+            v0 = mi * TILE
+            loads(Src.rows(W, v0 * ldb, V - v0, ldb), H, "fwd-skip A")
+            t0 = tile_list[2 * ni]
+            t1 = tile_list[2 * ni + 1] if 2 * ni + 1 < n_act else -1
+            loads(Src.rows2(h, t0 * SKIP * ldb, T - t0 * SKIP, (t1 if t1 >= 0 else t0) * SKIP * ldb,
+                            T - t1 * SKIP if t1 >= 0 else 0, ldb), H, "fwd-skip B")
+            for wn_, tl in ((0, t0), (1, t1)):
+                if tl < 0:
+                    continue
+                t = tl * SKIP + np.arange(128)
+                part.check((mi * T + t[t < T]) * 16, 16, "fwd-skip part")
     if not sample:
         transpose_model(h, T, H, ht, ld_t, esz, "h^T", tiles=tile_list[:n_act] if compact else None)
     pieces = span_pieces(S.active_spans(mask, 128))
