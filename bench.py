@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--skip-fwd", action="store_true",
                    help="forward over active token tiles only (FLH_FWD_SKIP_INACTIVE; the default is "
                         "the dense forward)")
+    p.add_argument("--padded-tail", action="store_true",
+                   help="probe: the padded-staging baseline of the live-width vocabulary split "
+                        "(FLH_BWD_PADDED_TAIL; same results)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the headline run: backward time of the stress workload at its "
                         "active fractions, fitted against the active-tile fraction")
@@ -206,7 +209,7 @@ def main():
         lp, ent, lse = flh_forward(h, W, y, workspace=ws_f, meta=meta,
                                    skip_inactive=args.skip_fwd and not args.dense)
         dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
-                              skip_inactive_dw=args.skip_dw)
+                              skip_inactive_dw=args.skip_dw, padded_tail=args.padded_tail)
         return dH, dW
 
     if args.copy_calib_mib > 0:
@@ -292,7 +295,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
                    "active_frac": minfo["active_frac"], "mask_seed": minfo["seed"],
                    "dense_fallback": bool(args.dense), "skip_inactive_dw": bool(args.skip_dw),
-                   "skip_inactive_fwd": bool(args.skip_fwd)},
+                   "skip_inactive_fwd": bool(args.skip_fwd), "padded_tail": bool(args.padded_tail)},
         "pct_peak_method": F_method / (ms * 1e-3) / peak,
         "work": {"A": A, "T_at128": int(T_at), "T_sp": int(T_sp), "spans": len(spans),
                  "F_method_tflop": F_method / 1e12, "F_dense_tflop": 4 * pass_flops * T / 1e12},

@@ -19,7 +19,8 @@ STATUS_NAMES = {
 }
 FLH_F32, FLH_BF16 = 0, 1
 OP_SPANS, OP_FORWARD, OP_BACKWARD = 0, 1, 2
-FLH_BWD_SKIP_INACTIVE_DW = 1  # flh_backward_ex option (include/flh.h)
+FLH_BWD_SKIP_INACTIVE_DW = 1  # flh_backward_ex options (include/flh.h)
+FLH_BWD_PADDED_TAIL = 2
 FLH_FWD_SKIP_INACTIVE = 1  # flh_forward_ex option
 
 

@@ -293,7 +293,10 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
                            int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
                            size_t ws_bytes, void *stream, uint32_t flags) {
   if (!dtype_ok(dt)) return FLH_E_DTYPE;
-  if (flags & ~(uint32_t)FLH_BWD_SKIP_INACTIVE_DW) return FLH_E_UNSUPPORTED;
+  if (flags & ~(uint32_t)(FLH_BWD_SKIP_INACTIVE_DW | FLH_BWD_PADDED_TAIL)) return FLH_E_UNSUPPORTED;
+  // the padded probe computes tiles with no live vocabulary row, which the fp32 load
+  // path cannot address (it clamps onto the last live row)
+  if ((flags & FLH_BWD_PADDED_TAIL) && dt != FLH_BF16) return FLH_E_UNSUPPORTED;
   if (!h || !W || !targets || !lse || !entropy || !d_hidden || !d_weight || !ws) return FLH_E_NULL;
   const int32_t S = split_or_default(vocab_split);
   if (!dims_ok(dt, T, H, V) || S <= 0 || S % kTile != 0) return FLH_E_SHAPE;
@@ -367,14 +370,15 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
     const int64_t ld_prev = a.ld_d;
     a.v_base = sp * S;
     a.Ws = (int32_t)Ws;
-    a.ld_d = (int32_t)pad_ld(Ws);
+    a.Ws_grid = (flags & FLH_BWD_PADDED_TAIL) ? (V < S ? V : S) : Ws;
+    a.ld_d = (int32_t)pad_ld(a.Ws_grid);
     a.first_split = sp == 0;
     // inactive token tiles: zero staging once per layout (the first split is the widest)
     a.zero_vm = sp == 0 && !a.compact_dw;
     a.zero_tm = sp == 0 || a.ld_d != ld_prev;
     a.Wt = base + L.Wt + (size_t)sp * (size_t)H * (size_t)L.ld_wt * (size_t)elt_size(dt);
     const int32_t tag = (int32_t)sp;
-    const int64_t v_tiles = cdiv(Ws, kTile);
+    const int64_t v_tiles = cdiv(a.Ws_grid, kTile);
     s = run(kIdDlogits, tag, st, [&] {
       return launch_gemm((int)dt, kDlogits, a, grid_for(v_tiles * cdiv(a.n_skip_tiles, 2), cus), st);
     });
@@ -385,7 +389,7 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
     });
     if (s != FLH_OK) return s;
     s = run(kIdDweight, tag, st, [&] {
-      return launch_gemm((int)dt, kDweight, a, grid_for(cdiv(Ws, kTile) * h_tiles, cus), st);
+      return launch_gemm((int)dt, kDweight, a, grid_for(v_tiles * h_tiles, cus), st);
     });
     if (s != FLH_OK) return s;
   }

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     n_tiles = cdiv(uni(a.counts[0]), 2);  // pairs of active token tiles
     K = a.H;
   } else if constexpr (KIND == kDlogits) {
-    m_tiles = cdiv(a.Ws, kTile);
+    m_tiles = cdiv(a.Ws_grid, kTile);
     n_pairs_gemm = cdiv(uni(a.counts[0]), 2);
     n_pairs_all = (a.zero_tm || a.zero_vm) ? cdiv(a.n_skip_tiles, 2) : n_pairs_gemm;
     n_tiles = n_pairs_gemm;
@@ -261,9 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   } else if constexpr (KIND == kDhidden) {
     m_tiles = uni(a.counts[1]);
     n_tiles = cdiv(a.H, kTile);
-    K = a.Ws;
+    K = a.Ws_grid;
   } else {
-    m_tiles = cdiv(a.Ws, kTile);
+    m_tiles = cdiv(a.Ws_grid, kTile);
     n_tiles = cdiv(a.H, kTile);
     K = a.compact_dw ? (int64_t)uni(a.counts[0]) * kSkipTile : a.T;
   }
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t mi = z % m_tiles;
         const int64_t p = n_pairs_gemm + z / m_tiles;
         const int64_t c0 = mi * kTile;
-        const int64_t c1 = imin(c0 + kTile, cdiv(a.Ws, kPer) * kPer);
+        const int64_t c1 = imin(c0 + kTile, cdiv(a.Ws_grid, kPer) * kPer);
         // token-major staging: rows of the pair's tokens, columns [c0, c1)
         constexpr int kChunks = kTile / kPer;
         char *Dw = const_cast<char *>(Dp);
@@ -877,7 +877,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     } else if constexpr (KIND == kDlogits) {
       const int64_t v_tile = mi * kTile;  // split-local first column
       const int n_live = (int)imin(a.Ws - v_tile, kTile);
-      const int n_cols = (int)imin(cdiv(a.Ws, kPer) * kPer - v_tile, kTile);  // written columns
+      const int n_cols = (int)imin(cdiv(a.Ws_grid, kPer) * kPer - v_tile, kTile);  // written columns
       const int64_t t_pad = cdiv(a.T, kPer) * kPer;  // tokens written, zero padding included
       // the pair's two token tiles (the second may be missing)
       const int64_t n_act = uni(a.counts[0]);  // active token tiles

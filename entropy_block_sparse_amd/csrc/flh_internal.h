@@ -68,6 +68,10 @@ struct GemmArgs {
   // h^T hold just the active 128-token tiles, in the order of the tile list (column
   // 128 r + j is token j of the r-th active tile), and dW contracts over those.
   int32_t compact_dw;
+  // Split width the launches and the staging use: the live width W_s, or (the padded
+  // baseline the live width replaces, a measurement probe) the widest split's width;
+  // operand reads and dW stores stay bounded by W_s.
+  int64_t Ws_grid;
   int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
                            // in flight on one XCD form a group_m x 32/group_m block)
   void *dW;                // [V][H]

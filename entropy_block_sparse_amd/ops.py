@@ -14,8 +14,8 @@ from typing import List, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import (FLH_BF16, FLH_BWD_SKIP_INACTIVE_DW, FLH_F32, FLH_FWD_SKIP_INACTIVE, OP_BACKWARD, OP_FORWARD,
-                   ActiveMeta, check, lib)
+from ._lib import (FLH_BF16, FLH_BWD_PADDED_TAIL, FLH_BWD_SKIP_INACTIVE_DW, FLH_F32, FLH_FWD_SKIP_INACTIVE,
+                   OP_BACKWARD, OP_FORWARD, ActiveMeta, check, lib)
 
 DEFAULT_MAX_GAP = 128
 DEFAULT_VOCAB_SPLIT = 16384
@@ -161,11 +161,14 @@ def flh_backward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
                  entropy: torch.Tensor, grad_logprob: Optional[torch.Tensor],
                  grad_entropy: Optional[torch.Tensor], loss_mask: Optional[torch.Tensor] = None,
                  meta: Optional[ActiveMetaTensors] = None, vocab_split: int = 0,
-                 workspace: Optional[torch.Tensor] = None, skip_inactive_dw: bool = False):
+                 workspace: Optional[torch.Tensor] = None, skip_inactive_dw: bool = False,
+                 padded_tail: bool = False):
     """Returns (d_hidden [T,H], d_weight [V,H]) in the dtype of h.
 
     skip_inactive_dw: flh_backward_ex's FLH_BWD_SKIP_INACTIVE_DW (the weight gradient
-    over active token tiles only; same result)."""
+    over active token tiles only; same result).
+    padded_tail: FLH_BWD_PADDED_TAIL, the padded-staging baseline of the live-width split
+    (a measurement probe; same result)."""
     _require_cuda(h, W, targets, lse, entropy, grad_logprob, grad_entropy, loss_mask)
     h, W = h.contiguous(), W.contiguous()
     targets = targets.to(torch.int64).contiguous()
@@ -182,11 +185,12 @@ def flh_backward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
         raise ValueError("invalid sizes or vocab_split")
     ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
     mp = ctypes.byref(meta.struct) if meta is not None else None
-    if skip_inactive_dw:
+    flags = (FLH_BWD_SKIP_INACTIVE_DW if skip_inactive_dw else 0) | (FLH_BWD_PADDED_TAIL if padded_tail else 0)
+    if flags:
         check(lib().flh_backward_ex(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), _ptr(lse),
                                     _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V,
                                     int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
-                                    _stream(dev), FLH_BWD_SKIP_INACTIVE_DW), "flh_backward_ex")
+                                    _stream(dev), flags), "flh_backward_ex")
     else:
         check(lib().flh_backward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), _ptr(lse),
                                  _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V,

@@ -218,7 +218,13 @@ enum {
    * method lists after the dense weight gradient, which the pages keep dense on
    * purpose (SkyRL #2376, "How it works": weight gradients stay a dense
    * contraction).  Has no effect when meta is NULL (every tile is active). */
-  FLH_BWD_SKIP_INACTIVE_DW = 1u
+  FLH_BWD_SKIP_INACTIVE_DW = 1u,
+  /* Measurement probe of the baseline that the live-width split replaces (SkyRL #2376,
+   * "Performance": live-width final vocabulary split against padded staging): every
+   * split, the last included, is staged and launched at the widest split's width
+   * min(V, vocab_split), with the padding columns zero.  The results equal the default's
+   * bitwise; only the time differs.  bf16 only (FLH_E_UNSUPPORTED for fp32). */
+  FLH_BWD_PADDED_TAIL = 2u
 };
 
 /*

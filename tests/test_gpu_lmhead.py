@@ -243,3 +243,37 @@ def test_forward_skip_inactive_matches_dense(dtype, T, H, V, split, kind):
     out = flh_backward(h, W, y, sparse[2], sparse[1], g_lp, g_ent, m, meta, split)
     torch.cuda.synchronize()
     assert torch.equal(ref[0], out[0]) and torch.equal(ref[1], out[1])
+
+
+@pytest.mark.parametrize("T,H,V,split,skip_dw", [(1000, 520, 5000, 2048, False), (777, 128, 2600, 1024, False),
+                                                 (1000, 520, 5000, 2048, True), (600, 64, 900, 4096, False)])
+def test_padded_tail_probe_matches_live_width(T, H, V, split, skip_dw):
+    """The padded-staging baseline (FLH_BWD_PADDED_TAIL: the last split staged and launched
+    at the full split width, padding zero) gives the live-width results bitwise: the
+    padding adds zero products only and no store outside the live rows."""
+    dev = cuda_device()
+    announce(f"padded tail T={T} H={H} V={V} split={split} skip_dw={skip_dw}")
+    mask = bursty_mask(T, 51)
+    h, W, y = [x.to(dev) for x in make_tensors(T, H, V, "bf16", 52)]
+    m = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m)
+    a, b = make_upstream(mask)
+    g_lp, g_ent = torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev)
+    lp, ent, lse = flh_forward(h, W, y)
+    live = flh_backward(h, W, y, lse, ent, g_lp, g_ent, m, meta, split, skip_inactive_dw=skip_dw)
+    padded = flh_backward(h, W, y, lse, ent, g_lp, g_ent, m, meta, split, skip_inactive_dw=skip_dw,
+                          padded_tail=True)
+    torch.cuda.synchronize()
+    assert torch.equal(live[0], padded[0]) and torch.equal(live[1], padded[1])
+
+
+def test_padded_tail_probe_rejects_fp32():
+    from entropy_block_sparse_amd._lib import FlhError
+    dev = cuda_device()
+    T, H, V = 256, 64, 700
+    h, W, y = [x.to(dev) for x in make_tensors(T, H, V, "f32", 53)]
+    m = torch.ones(T, dtype=torch.uint8, device=dev)
+    meta = flh_spans_build(m)
+    lp, ent, lse = flh_forward(h, W, y)
+    with pytest.raises(FlhError):
+        flh_backward(h, W, y, lse, ent, None, None, m, meta, 256, padded_tail=True)

@@ -227,7 +227,7 @@ def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols, ni=0,
         Dt.check(((v0 + mb[ok] + li[ok]) * ld_t + t[ok]) * 2, 16, "dlg store^T (LDS)")
 
 
-def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
+def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False):
     """Walks every (sampled) workgroup tile of the four contractions and checks loads
     (per the fp32 or bf16 load path) and epilogue stores against the buffers."""
     kper = 16 // esz
@@ -247,7 +247,7 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
     dW = Buf("dW", V * H * esz)
 
     def loads(src, K, what):
-        assert src.n[0] >= 1, f"{what}: a tile's first segment always has rows"
+        assert src.n[0] >= 1 or (padded and v2), f"{what}: a tile's first segment always has rows"
         if v2:
             rsrc_v2(src, K, what)
         else:
@@ -295,15 +295,16 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
     for sp in _pick(cdiv(V, S_split), sample):
         Ws = min(S_split, V - sp * S_split)
         v_base = sp * S_split
-        ld_d = pad_ld(Ws)
-        w_pad = cdiv(Ws, kper) * kper  # columns of the token-major staging that are written
+        Ws_grid = w_max if padded else Ws  # the launches' and the staging's width
+        ld_d = pad_ld(Ws_grid)
+        w_pad = cdiv(Ws_grid, kper) * kper  # columns of the token-major staging that are written
         assert ld_d <= ld_max and w_pad <= ld_wt and w_pad <= ld_d and t_pad <= ld_t
         # ---- d-logits ----
-        m_tiles = cdiv(Ws, TILE)
+        m_tiles = cdiv(Ws_grid, TILE)
         n_pairs_gemm, n_pairs_all = cdiv(n_act, 2), cdiv(n_skip, 2)
         for mi in _pick(m_tiles, sample):
             v0 = mi * TILE
-            assert v0 <= Ws - 1
+            assert v0 <= Ws_grid - 1
             n_live, n_cols = min(Ws - v0, TILE), min(w_pad - v0, TILE)
             wb = (v_base + v0) * ldb
             for ni in _pick(n_pairs_gemm, sample):
@@ -361,9 +362,9 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
             pn = [p[1] - p[0] for p in tp] + [0] * (PIECES_PER_TILE - len(tp))
             assert all(1 <= x <= PIECE for x in pn[:len(tp)])
             n0 = ni * TILE
-            loads(Src(D, [x * ldd for x in ps], pn, ldd), Ws, "dh A")
+            loads(Src(D, [x * ldd for x in ps], pn, ldd), Ws_grid, "dh A")
             wt = (sp * H + n0) * ldw
-            loads(Src.rows(Wt, wt, H - n0, ldw), Ws, "dh B")
+            loads(Src.rows(Wt, wt, H - n0, ldw), Ws_grid, "dh B")
             if v2:
                 # read-modify-write of whole rows, 16 bytes per lane (4 columns), per
                 # 32-row block = one piece
@@ -386,7 +387,7 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False):
                     acc.check((t[ok] * H + n[ok]) * 4, 4, "dh store")
         # ---- dWeight: A = vocabulary-major staging rows, B = h^T rows ----
         ldt = ld_t * esz
-        for mi, ni in itertools.product(_pick(cdiv(Ws, TILE), sample), _pick(cdiv(H, TILE), sample)):
+        for mi, ni in itertools.product(_pick(cdiv(Ws_grid, TILE), sample), _pick(cdiv(H, TILE), sample)):
             v0, n0 = mi * TILE, ni * TILE
             K_dw = n_act * SKIP if compact else T
             if K_dw > 0:
@@ -461,6 +462,8 @@ def test_kernel_addressing_full_workloads_sampled(cid):
     model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2 if cfg.dtype == "bf16" else 4, mask, sample=True)
     model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2 if cfg.dtype == "bf16" else 4, mask, sample=True,
           compact=True)
+    if cfg.dtype == "bf16":
+        model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2, mask, sample=True, padded=True)
 
 
 # ---- bf16 path: LDS-direct buffer loads ------------------------------------------------
@@ -475,6 +478,7 @@ def test_bf16_descriptors_in_bounds(T, H, V, S_split):
     for mask in (np.ones(T, np.uint8), (rng.random(T) < 0.4).astype(np.uint8), np.zeros(T, np.uint8)):
         model(T, H, V, S_split, 2, mask)
         model(T, H, V, S_split, 2, mask, compact=True)
+        model(T, H, V, S_split, 2, mask, padded=True)
 
 
 # ---- tile schedule: XCD-aware remap and grouped rasterization ---------------------------
