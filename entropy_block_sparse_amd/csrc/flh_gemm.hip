@@ -134,6 +134,33 @@ template <> struct Mma<float> {
   static __device__ __forceinline__ void run_in_place(f32x4 &c, u32x4 a, u32x4 b) { run(c, a, b); }
 };
 
+// x combined with its value in lane l ^ 16 (resp. l ^ 32) under a symmetric operation,
+// through the in-register lane swaps of gfx950: v_permlane16_swap (32_swap) of x with
+// itself leaves, in every lane, x of the lower and of the upper lane of the pair.  (A
+// shuffle would take an LDS round trip per step.)
+__device__ __forceinline__ void lanes_x16(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void lanes_x32(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_over_x16_x32(float x) {
+  float a, b;
+  lanes_x16(x, a, b);
+  lanes_x32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_over_x16_x32(float x) {
+  float a, b;
+  lanes_x16(x, a, b);
+  lanes_x32(a + b, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
@@ -815,8 +842,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             for (int e = 1; e < 8; ++e) m4[c] = fmaxf(m4[c], z_at(c + 4 * (e >> 2), j, e & 3));
           }
           float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          mx = max_over_x16_x32(mx);  // the column's 4 lane groups
           const float nm2 = -mx * kLog2e;
           float s4[4], u4[4];
 #pragma unroll
@@ -833,10 +859,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           }
           float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
           float u = (u4[0] + u4[1]) + (u4[2] + u4[3]);
-          s += __shfl_xor(s, 16);
-          u += __shfl_xor(u, 16);
-          s += __shfl_xor(s, 32);
-          u += __shfl_xor(u, 32);
+          s = sum_over_x16_x32(s);
+          u = sum_over_x16_x32(u);
           u *= kLn2;
           if (!wave_live) {
             mx = kNegInf;
