@@ -140,6 +140,34 @@ def test_backward_validation():
     assert _bwd(nbytes=1000) == E["FLH_E_WORKSPACE"]
 
 
+def _fwd_ex(flags, meta="ok", dt=1, T=512, H=256, V=4096, nbytes=1 << 40):
+    m = _meta(T=512) if meta == "ok" else meta
+    mp = ctypes.byref(m) if m is not None else None
+    return lib().flh_forward_ex(dt, FAKE, FAKE, FAKE, T, H, V, FAKE, FAKE, FAKE, mp, FAKE, nbytes, None,
+                                flags)
+
+
+def _bwd_ex(flags, dt=1):
+    m = _meta(T=512)
+    return lib().flh_backward_ex(dt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(m),
+                                 512, 256, 4096, 0, FAKE, FAKE, FAKE, 1 << 40, None, flags)
+
+
+def test_option_entry_point_validation():
+    from entropy_block_sparse_amd._lib import FLH_BWD_PADDED_TAIL, FLH_FWD_SKIP_INACTIVE
+    # unknown option bits are refused before anything runs
+    assert _fwd_ex(1 << 5) == E["FLH_E_UNSUPPORTED"]
+    assert _bwd_ex(1 << 7) == E["FLH_E_UNSUPPORTED"]
+    # the forward over active tiles needs metadata of this T and tile height
+    assert _fwd_ex(FLH_FWD_SKIP_INACTIVE, meta=None) == E["FLH_E_META"]
+    assert _fwd_ex(FLH_FWD_SKIP_INACTIVE, meta=_meta(T=511)) == E["FLH_E_META"]
+    assert _fwd_ex(FLH_FWD_SKIP_INACTIVE, meta=_meta(T=512, tm=64)) == E["FLH_E_META"]
+    assert _fwd_ex(FLH_FWD_SKIP_INACTIVE, meta=_meta(T=512, bits=None)) == E["FLH_E_NULL"]
+    assert _fwd_ex(FLH_FWD_SKIP_INACTIVE, nbytes=1000) == E["FLH_E_WORKSPACE"]
+    # the padded-staging probe is bf16 only
+    assert _bwd_ex(FLH_BWD_PADDED_TAIL, dt=0) == E["FLH_E_UNSUPPORTED"]
+
+
 def test_python_binding_names_match_abi():
     import entropy_block_sparse_amd as pkg
     for n in ("flh_spans_build", "flh_forward", "flh_backward", "flh_workspace_bytes",
