@@ -181,7 +181,7 @@ def cpu_baseline(h, W, y, mask, a, b, n_tok):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     if args.sweep:
         sweep(args)

@@ -68,7 +68,7 @@ typedef enum {
   FLH_E_ALIGN = 4,       /* a matrix pointer or the workspace is misaligned          */
   FLH_E_WORKSPACE = 5,   /* ws_bytes smaller than flh_workspace_bytes()              */
   FLH_E_META = 6,        /* active metadata inconsistent with this call              */
-  FLH_E_UNSUPPORTED = 7, /* valid request this build does not support                */
+  FLH_E_UNSUPPORTED = 7, /* valid request the library does not support               */
   FLH_E_HIP = 8          /* a HIP runtime call or kernel launch failed               */
 } flh_status;
 
