@@ -680,9 +680,21 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // A stage is two K steps of 64 MFMAs, (i, j) = (p / 8, p % 8) for MFMA p.  A
       // scheduling fence after every MFMA keeps the order written here.
       //
+      // Right after the barrier that publishes a stage every wave reads at once, so the
+      // LDS is busiest there.  Only the first kPostReads fragments of the stage's slice 0
+      // (A0, B0..B7, A1) are read then; A2..A7 follow in the first step, fragment A(i)
+      // beside MFMA 8 (i - 2), a row of 8 MFMAs before its row starts.
+      constexpr int kPostReads = 10;
+      static_assert(kPostReads >= 10 && kPostReads <= 16, "A(i), i >= 2, are read in the first step");
+      auto read_slice0_a = [&](int s, int p, u32x4 (&fa)[8]) {  // read p (>= 9) of slice 0 = A(p - 8)
+        fa[p - 8] = read_frag(smem + (s & 1) * kStage, wm * 128, p - 8, 0);
+      };
+      //
       // First step (fragments ca, cb): beside MFMA 2k + 1 (k < 16) fragment read k of
       // slice 1 of this stage into (na, nb); beside MFMA 2k, load k of stage ls (if
-      // ls >= 0; A then B); after the last load, the L2 prefetch of stage pfs.
+      // ls >= 0; A then B); after the last load, the L2 prefetch of stage pfs; beside
+      // MFMA 8 m, the read of A(m + 2) of slice 0 into ca unless it was read after the
+      // barrier.
       // `last`: the tile's last stage, with the compiler's MFMA (see Mma).
       auto mma = [&](bool last, int p, const u32x4 (&ca)[8], const u32x4 (&cb)[8]) {
         if (last)
@@ -690,10 +702,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         else
           Mma<T>::run_in_place(acc[p >> 3][p & 7], ca[p >> 3], cb[p & 7]);
       };
-      auto kstep0 = [&](const u32x4 (&ca)[8], const u32x4 (&cb)[8], u32x4 (&na)[8], u32x4 (&nb)[8],
+      auto kstep0 = [&](u32x4 (&ca)[8], const u32x4 (&cb)[8], u32x4 (&na)[8], u32x4 (&nb)[8],
                         int rs, int ls, int pfs, bool last) {
 #pragma unroll
         for (int p = 0; p < 64; ++p) {
+          if ((p & 7) == 0 && 10 + (p >> 3) >= kPostReads && 10 + (p >> 3) < 16)
+            read_slice0_a(rs, 10 + (p >> 3), ca);
           if (p < 32 && (p & 1)) read_one(rs, 1, p >> 1, na, nb);
           if (ls >= 0 && p < 32 && !(p & 1)) issue_one(ls, (p >> 1) >> 3, (p >> 1) & 7);
           if (pfs >= 0 && p == 32) issue_pf(pfs);
@@ -702,9 +716,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
       };
       // Second step: kBarAt MFMAs; then, if there is a next stage, wait for its loads,
-      // publish it (barrier) and read its slice 0 into (na, nb), one fragment beside
-      // each of the remaining MFMAs.
-      constexpr int kBarAt = 48;
+      // publish it (barrier) and read the first kPostReads fragments of its slice 0 into
+      // (na, nb), one beside each of the remaining MFMAs.
+      constexpr int kBarAt = 52;
+      static_assert(64 - kBarAt >= kPostReads, "one read per MFMA after the barrier");
       auto kstep1 = [&](const u32x4 (&ca)[8], const u32x4 (&cb)[8], u32x4 (&na)[8], u32x4 (&nb)[8],
                         bool next, int ns) {
 #pragma unroll
@@ -720,14 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
 #pragma unroll
         for (int p = kBarAt; p < 64; ++p) {
-          if (next) {
-            const int r0 = p - kBarAt, nr = 64 - kBarAt;  // reads spread over the rest
-            if (nr >= 16) {
-              if (r0 < 16) read_one(ns, 0, r0, na, nb);
-            } else {
-              for (int r = r0 * 16 / nr; r < (r0 + 1) * 16 / nr; ++r) read_one(ns, 0, r, na, nb);
-            }
-          }
+          if (next && p - kBarAt < kPostReads) read_one(ns, 0, p - kBarAt, na, nb);
           mma(!next, p, ca, cb);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -742,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       __builtin_amdgcn_s_barrier();
       u32x4 F0a[8], F0b[8], F1a[8], F1b[8];
 #pragma unroll
-      for (int p = 0; p < 16; ++p) read_one(0, 0, p, F0a, F0b);
+      for (int p = 0; p < kPostReads; ++p) read_one(0, 0, p, F0a, F0b);
       __builtin_amdgcn_sched_barrier(0);
 
       // Stage kt: stage kt+1 streams into the other buffer (which held stage kt-1,
