@@ -333,14 +333,16 @@ __global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, co
       if (act) {
         const float4 x0 = *reinterpret_cast<const float4 *>(acc + t * H + c);
         const float4 x1 = *reinterpret_cast<const float4 *>(acc + t * H + c + 4);
-        auto rne = [](float f) {
-          const uint32_t u = __float_as_uint(f);
-          return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        // pairs rounded to bf16 (nearest, ties to even) by v_cvt_pk_bf16_f32
+        auto rne2 = [](float lo, float hi) {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
         };
-        w[0] = rne(x0.x) | (rne(x0.y) << 16);
-        w[1] = rne(x0.z) | (rne(x0.w) << 16);
-        w[2] = rne(x1.x) | (rne(x1.y) << 16);
-        w[3] = rne(x1.z) | (rne(x1.w) << 16);
+        w[0] = rne2(x0.x, x0.y);
+        w[1] = rne2(x0.z, x0.w);
+        w[2] = rne2(x1.x, x1.y);
+        w[3] = rne2(x1.z, x1.w);
       }
       *reinterpret_cast<uint4 *>(dh + t * H + c) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {

@@ -161,20 +161,23 @@ __device__ __forceinline__ float sum_over_x16_x32(float x) {
   return a + b;
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two floats rounded to bf16 (to nearest, ties to even), lo in bits 0..15: one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 __device__ __forceinline__ void store4(uint16_t *p, float a, float b, float c, float d) {
   u32x2 v;
-  v.x = bf16_rne(a) | (bf16_rne(b) << 16);
-  v.y = bf16_rne(c) | (bf16_rne(d) << 16);
+  v.x = bf16x2_rne(a, b);
+  v.y = bf16x2_rne(c, d);
   *reinterpret_cast<u32x2 *>(p) = v;
 }
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
   *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
-__device__ __forceinline__ void store1(uint16_t *p, float a) { *p = (uint16_t)bf16_rne(a); }
+__device__ __forceinline__ void store1(uint16_t *p, float a) { *p = (uint16_t)bf16x2_rne(a, 0.f); }
 __device__ __forceinline__ void store1(float *p, float a) { *p = a; }
 
 // Merge two (max, sum exp(z - max), sum exp(z - max)(z - max)) states.
@@ -787,8 +790,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // columns cb .. cb + 7, or -1 to skip them.
     auto ls_put4 = [&](int col, int c0, float d0, float d1, float d2, float d3) {
       u32x2 v;
-      v.x = bf16_rne(d0) | (bf16_rne(d1) << 16);
-      v.y = bf16_rne(d2) | (bf16_rne(d3) << 16);
+      v.x = bf16x2_rne(d0, d1);
+      v.y = bf16x2_rne(d2, d3);
       *reinterpret_cast<u32x2 *>(smem + col * kLsPitch + c0 * 2) = v;
     };
     auto ls_store_rows = [&](char *dst, int64_t ld, int m_valid, auto &&colmap) {
