@@ -179,6 +179,12 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
 }
 __device__ __forceinline__ void store1(uint16_t *p, float a) { *p = (uint16_t)bf16x2_rne(a, 0.f); }
 __device__ __forceinline__ void store1(float *p, float a) { *p = a; }
+// 16-byte streaming store (nontemporal): for the d-logits staging of a split (a GiB at
+// the Llama-3-8B-like shape, far more than L2), written once and read by the next two
+// launches.  (For the weight gradient, measured slower than plain stores.)
+__device__ __forceinline__ void store16_nt(char *p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
 
 // Merge two (max, sum exp(z - max), sum exp(z - max)(z - max)) states.
 __device__ __forceinline__ void merge_state(float &M, float &s, float &u, float M2, float s2,
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const int64_t t = (int64_t)a.tile_list[e] * kSkipTile + (row & 127);
           const int64_t col = c0 + (int64_t)ch * kPer;
           if (t < a.T && col < c1)
-            *reinterpret_cast<u32x4 *>(Dw + (t * a.ld_d + col) * kEsz) = u32x4{0u, 0u, 0u, 0u};
+            store16_nt(Dw + (t * a.ld_d + col) * kEsz, u32x4{0u, 0u, 0u, 0u});
         }
         // vocabulary-major staging: rows v in [c0, min(c0 + 256, Ws)), the pair's
         // tokens including the zero padding up to a whole 16-byte chunk
@@ -343,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           if (e >= a.n_skip_tiles || v >= v1) continue;
           const int64_t t = (int64_t)a.tile_list[e] * kSkipTile + vec * kPer;
           if (t < cdiv(a.T, kPer) * kPer)
-            *reinterpret_cast<u32x4 *>(Dtw + (v * a.ld_t + t) * kEsz) = u32x4{0u, 0u, 0u, 0u};
+            store16_nt(Dtw + (v * a.ld_t + t) * kEsz, u32x4{0u, 0u, 0u, 0u});
         }
         continue;
       }
@@ -797,15 +803,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // names 4 consecutive rows (mb + 4 (i % 4)) of column line cb + i / 4 and receives
     // row mb + i over columns cb .. cb + 3; two reads give 8 columns, one 16-byte store.
     // A wave store writes 64 contiguous bytes of each of 16 rows.  Row m (< m_valid)
-    // goes to dst + m * ld elements; colmap(cb) gives the destination column of tile
-    // columns cb .. cb + 7, or -1 to skip them.
+    // goes to dst + m * ld elements (streaming stores if kNt); colmap(cb) gives the
+    // destination column of tile columns cb .. cb + 7, or -1 to skip them.
     auto ls_put4 = [&](int col, int c0, float d0, float d1, float d2, float d3) {
       u32x2 v;
       v.x = bf16x2_rne(d0, d1);
       v.y = bf16x2_rne(d2, d3);
       *reinterpret_cast<u32x2 *>(smem + col * kLsPitch + c0 * 2) = v;
     };
-    auto ls_store_rows = [&](char *dst, int64_t ld, int m_valid, auto &&colmap) {
+    auto ls_store_rows = [&](auto nt, char *dst, int64_t ld, int m_valid, auto &&colmap) {
+      constexpr bool kNt = decltype(nt)::value;
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       const int li = elane & 15, g4 = elane >> 4;
 #pragma unroll
@@ -820,8 +827,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
               (s16x4 __attribute__((address_space(3))) *)(src + 4 * kLsPitch));
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
           const int64_t c = colmap(k, cb);
-          if (c >= 0 && mb + li < m_valid)
-            *reinterpret_cast<u32x4 *>(dst + ((int64_t)(mb + li) * ld + c) * 2) = u32x4{l2.x, l2.y, h2.x, h2.y};
+          if (c >= 0 && mb + li < m_valid) {
+            char *p = dst + ((int64_t)(mb + li) * ld + c) * 2;
+            if constexpr (kNt)
+              store16_nt(p, u32x4{l2.x, l2.y, h2.x, h2.y});
+            else
+              *reinterpret_cast<u32x4 *>(p) = u32x4{l2.x, l2.y, h2.x, h2.y};
+          }
         }
       }
     };
@@ -995,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const int64_t tile = (tl >> 7) ? pt1 : pt0;
           const int64_t t = tile * kSkipTile + (tl & 127);
           if (tile >= 0 && t < a.T && cc < n_cols)
-            *reinterpret_cast<u32x4 *>(Db + (t * a.ld_d + cc) * 2) = v;
+            store16_nt(Db + (t * a.ld_d + cc) * 2, v);
         }
         // vocabulary-major: rows v of the split, tokens of the pair (zero padding to a
         // whole 16-byte chunk included)
@@ -1006,7 +1018,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t vcol1 =
             uni(pt1 < 0 ? -1 : (cpt ? (2 * ni + 1 < n_act ? (2 * ni + 1) * kSkipTile : -1) : pt1 * kSkipTile));
         const int64_t vlim = uni(cpt ? a.ld_t : t_pad);
-        ls_store_rows(Dvb, a.ld_t, n_live, [&](int k, int cb) -> int64_t {
+        ls_store_rows(std::true_type{}, Dvb, a.ld_t, n_live, [&](int k, int cb) -> int64_t {
           const int64_t base = (k >> 2) ? vcol1 : vcol0;  // cb / 128
           const int64_t c = base + (cb & 127);
           return (base >= 0 && c < vlim) ? c : -1;
@@ -1106,7 +1118,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           for (int i = 0; i < 8; ++i)
             ls_put4(col0 + j * 16, row0 + i * 16, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         __syncthreads();
-        ls_store_rows(reinterpret_cast<char *>(base), a.H, n_rows,
+        ls_store_rows(std::false_type{}, reinterpret_cast<char *>(base), a.H, n_rows,
                       [&](int, int cb) -> int64_t { return cb < n_cols ? cb : -1; });
       } else {
         const uint32_t ldw = (uint32_t)a.H;
