@@ -236,34 +236,59 @@ __device__ __forceinline__ bool tile_skipped(const uint32_t *bits, int64_t t) {
   return ((bits[i >> 5] >> (i & 31)) & 1u) == 0;
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(int64_t T, int64_t V,
-                                                      const float4 *__restrict__ part,
-                                                      const uint32_t *__restrict__ bits,
-                                                      float *__restrict__ logprob,
-                                                      float *__restrict__ entropy,
-                                                      float *__restrict__ lse) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
+// Merge of two (max, sum e^(z - max), sum e^(z - max) (z - max)) states into the first.
+__device__ __forceinline__ void merge_state(float &M, float &s, float &u, float M2, float s2, float u2) {
+  const float ninf = -__builtin_huge_valf();
+  const float Mn = fmaxf(M, M2);
+  if (Mn == ninf) return;
+  const bool e1 = (M == ninf), e2 = (M2 == ninf);
+  const float c1 = e1 ? 0.f : __expf(M - Mn);
+  const float c2 = e2 ? 0.f : __expf(M2 - Mn);
+  const float un = (e1 ? 0.f : c1 * (u + s * (M - Mn))) + (e2 ? 0.f : c2 * (u2 + s2 * (M2 - Mn)));
+  s = (e1 ? 0.f : s * c1) + (e2 ? 0.f : s2 * c2);
+  u = un;
+  M = Mn;
+}
+
+// Merge of the per-(vocabulary tile, token) softmax states into lse, entropy and
+// logprob = z_y - lse.  A workgroup of kCombWaves waves takes 64 consecutive tokens;
+// wave w merges the states of vocabulary tiles w, w + kCombWaves, ... (one coalesced
+// 1 KiB read across the wave per tile), then the first wave merges the waves' states of
+// each token through LDS in wave order, so the result is the same on every run.
+constexpr int kCombWaves = 16;
+__global__ __launch_bounds__(64 * kCombWaves) void combine_kernel(int64_t T, int64_t V,
+                                                                  const float4 *__restrict__ part,
+                                                                  const uint32_t *__restrict__ bits,
+                                                                  float *__restrict__ logprob,
+                                                                  float *__restrict__ entropy,
+                                                                  float *__restrict__ lse) {
+  __shared__ float4 st[kCombWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t tc = t < T ? t : T - 1;  // rows past T read the last token's states
+  const int64_t n_vt = (V + kTile - 1) / kTile;
+  float M = -__builtin_huge_valf(), s = 0.f, u = 0.f;
+#pragma unroll 4
+  for (int64_t vt = w; vt < n_vt; vt += kCombWaves) {
+    const float4 p = part[vt * T + tc];
+    merge_state(M, s, u, p.x, p.y, p.z);
+  }
+  st[w][lane] = make_float4(M, s, u, 0.f);
+  __syncthreads();
+  if (w != 0 || t >= T) return;
   if (tile_skipped(bits, t)) {
     lse[t] = 0.f;
     entropy[t] = 0.f;
     logprob[t] = 0.f;
     return;
   }
-  const float ninf = -__builtin_huge_valf();
-  const int64_t n_vt = (V + kTile - 1) / kTile;
-  float M = ninf, s = 0.f, u = 0.f;
-  for (int64_t vt = 0; vt < n_vt; ++vt) {
-    const float4 p = part[vt * T + t];
-    const float Mn = fmaxf(M, p.x);
-    if (Mn == ninf) continue;
-    const bool e1 = (M == ninf), e2 = (p.x == ninf);
-    const float c1 = e1 ? 0.f : __expf(M - Mn);
-    const float c2 = e2 ? 0.f : __expf(p.x - Mn);
-    const float un = (e1 ? 0.f : c1 * (u + s * (M - Mn))) + (e2 ? 0.f : c2 * (p.z + p.y * (p.x - Mn)));
-    s = (e1 ? 0.f : s * c1) + (e2 ? 0.f : p.y * c2);
-    u = un;
-    M = Mn;
+  M = st[0][lane].x;
+  s = st[0][lane].y;
+  u = st[0][lane].z;
+#pragma unroll
+  for (int k = 1; k < kCombWaves; ++k) {
+    const float4 q = st[k][lane];
+    merge_state(M, s, u, q.x, q.y, q.z);
   }
   const float ls = __logf(s);
   const float l = M + ls;
@@ -385,8 +410,8 @@ hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void
                        skip_bits, logprob);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = (T + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, T, V,
+  const int64_t blocks = (T + 63) / 64;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(64 * kCombWaves), 0, st, T, V,
                      reinterpret_cast<const float4 *>(part), skip_bits, logprob, entropy, lse);
   return hipGetLastError();
 }
