@@ -368,8 +368,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int64_t x = b & 7, q = n_round >> 3, rem8 = n_round & 7;
       L = r * G + x * q + imin(x, rem8) + (b >> 3);
     }
+    // Group height: 8 tiles along M (an 8 x 4 block per XCD) for the forward and the
+    // d-logits, 4 (4 x 8) for the hidden and weight gradients, whose K (a split's width,
+    // all tokens) is far longer -- measured per kind on the Llama-3-8B-like head.
+    constexpr int64_t kGroupM = (KIND == kDhidden || KIND == kDweight) ? 4 : 8;
     int64_t mi, ni;
-    group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : 8, mi, ni);
+    group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : kGroupM, mi, ni);
 
     if constexpr (KIND == kDweight) {
       if (K == 0) {  // weight gradient over no active token tile (compact form): zeros

@@ -507,8 +507,9 @@ def _tile_of(item, n_gemm, G, m_tiles, n_tiles, GM=8):
 def test_tile_schedule_is_a_bijection(m_tiles, n_tiles, G):
     """Every workgroup tile of a launch is computed exactly once, whatever the grid."""
     n_gemm = m_tiles * n_tiles
-    seen = [_tile_of(item, n_gemm, G, m_tiles, n_tiles) for item in range(n_gemm)]
-    assert sorted(seen) == [(mi, ni) for mi in range(m_tiles) for ni in range(n_tiles)]
+    for GM in (8, 4):  # the group heights the kernels use
+        seen = [_tile_of(item, n_gemm, G, m_tiles, n_tiles, GM) for item in range(n_gemm)]
+        assert sorted(seen) == [(mi, ni) for mi in range(m_tiles) for ni in range(n_tiles)]
     # with the remap, the tiles one XCD holds in a round are a contiguous run of ids
     if G % 8 == 0 and n_gemm > 8:
         r0 = min(G, n_gemm)
