@@ -628,10 +628,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // measured 1.5% faster on dWeight than shares laid out for that block.  The load
       // goes out after the stage's real loads, so the wait for those can leave it in
       // flight (vector loads complete in order).
-      // The forward kernel gains nothing from it and is short of scalar registers, so
-      // it runs without.
+      // Measured per kind at two stages ahead: without it d-logits is 7% and dWeight 15%
+      // slower; the forward gains about 1%.
       constexpr int kPfAhead = 2;  // 1 was as slow as none, 3 4% slower on dWeight
-      constexpr bool kPrefetch = KIND != kFwd && KIND != kFwdSkip;
+      constexpr bool kPrefetch = true;
       __amdgpu_buffer_rsrc_t rpf = rsrc(Wp, 0);
       uint32_t pf_vo = 0;
       if constexpr (kPrefetch) {
