@@ -718,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // clocks) arrive at over twice that rate and queue, while every load still hitting
       // L2 leaves the loop almost as slow as it is.  Loads later in the step have less time
       // to land before the barrier that publishes their stage.
-      constexpr int kLoadEvery = 3;
+      constexpr int kLoadEvery = 4;  // 2: 3% slower per step; 3: 0.4% slower
       static_assert(15 * kLoadEvery < 64, "a stage's loads are issued in its first step");
       constexpr int kPfAt = 16 * kLoadEvery < 64 ? 16 * kLoadEvery : 63;
       // `last`: the tile's last stage, with the compiler's MFMA (see Mma).
