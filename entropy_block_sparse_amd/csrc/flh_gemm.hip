@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       };
       //
       // First step (fragments ca, cb): beside MFMA 2k + 1 (k < 16) fragment read k of
-      // slice 1 of this stage into (na, nb); beside MFMA kLoadEvery * k, load k of stage
+      // slice 1 of this stage into (na, nb); beside MFMA kLoadEvery * k + 1, load k of stage
       // ls (if ls >= 0; A then B); after the last load, the L2 prefetch of stage pfs;
       // beside MFMA 8 m, the read of A(m + 2) of slice 0 into ca unless it was read after
       // the barrier.
@@ -719,8 +719,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // L2 leaves the loop almost as slow as it is.  Loads later in the step have less time
       // to land before the barrier that publishes their stage.
       constexpr int kLoadEvery = 4;  // 2: 3% slower per step; 3: 0.4% slower
-      static_assert(15 * kLoadEvery < 64, "a stage's loads are issued in its first step");
+      static_assert(15 * kLoadEvery + 1 < 64, "a stage's loads are issued in its first step");
       constexpr int kPfAt = 16 * kLoadEvery < 64 ? 16 * kLoadEvery : 63;
+      static_assert(kPfAt > 15 * kLoadEvery + 1, "the prefetch goes out after the stage's last load");
       // `last`: the tile's last stage, with the compiler's MFMA (see Mma).
       auto mma = [&](bool last, int p, const u32x4 (&ca)[8], const u32x4 (&cb)[8]) {
         if (last)
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           if ((p & 7) == 0 && 10 + (p >> 3) >= kPostReads && 10 + (p >> 3) < 16)
             read_slice0_a(rs, 10 + (p >> 3), ca);
           if (p < 32 && (p & 1)) read_one(rs, 1, p >> 1, na, nb);
-          if (ls >= 0 && p % kLoadEvery == 0 && p / kLoadEvery < 16)
+          if (ls >= 0 && p % kLoadEvery == 1 && p / kLoadEvery < 16)
             issue_one(ls, (p / kLoadEvery) >> 3, (p / kLoadEvery) & 7);
           if (pfs >= 0 && p == kPfAt) issue_pf(pfs);
           mma(last, p, ca, cb);
