@@ -308,11 +308,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       n_gemm + (KIND == kDlogits ? m_tiles * (n_pairs_all - n_pairs_gemm) : 0);
   const int64_t G = gridDim.x;
   const bool remap = (G % 8) == 0;
-  // Group height of the rasterization: 8 tiles along M (an 8 x 4 block per XCD) for the
-  // forward and the d-logits, 4 (4 x 8) for the hidden and weight gradients, whose K (a
-  // split's width, all tokens) is far longer -- measured per kind on the Llama-3-8B-like
-  // head.
-  constexpr int kGroupM = (KIND == kDhidden || KIND == kDweight) ? 4 : 8;
+  // Group height of the rasterization: 8 tiles along M, an 8 x 4 block per XCD.  (4 x 8
+  // blocks for the hidden and weight gradients were 2% faster on the Llama-3-8B-like head on
+  // one box, equal on another, and 12-19% slower on the stress shape, whose 28 column tiles
+  // do not divide into blocks of 8.)
+  constexpr int kGroupM = 8;
 
   const char *hp = reinterpret_cast<const char *>(a.h);
   const char *Wp = reinterpret_cast<const char *>(a.W);
@@ -623,14 +623,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // tile's eight 32-row segments segment 2 (n % 4) + w for wave w = 0, 1, of its B
       // tile's segment m % 8 (waves 2 and 3), where (m, n) is its tile; one 128-byte line
       // per row per stage (two lanes, one per 64-byte half), with 4-byte loads into a
-      // scratch corner of LDS.  For the 8 x 4 block that is each line once; for the 4 x 8
-      // block of the gradients every A segment twice and half the B segments, which
-      // measured 1.5% faster on dWeight than shares laid out for that block.  The load
+      // scratch corner of LDS: for the 8 x 4 block, each line once.  The load
       // goes out after the stage's real loads, so the wait for those can leave it in
       // flight (vector loads complete in order).
       // Measured per kind at two stages ahead: without it d-logits is 7% and dWeight 15%
       // slower; the forward gains about 1%.
-      constexpr int kPfAhead = 2;  // 1 was as slow as none, 3 4% slower on dWeight
+      constexpr int kPfAhead = 2;  // 1 was as slow as none, 3 4-7% slower on dWeight
       constexpr bool kPrefetch = true;
       __amdgpu_buffer_rsrc_t rpf = rsrc(Wp, 0);
       uint32_t pf_vo = 0;

@@ -507,7 +507,7 @@ def _tile_of(item, n_gemm, G, m_tiles, n_tiles, GM=8):
 def test_tile_schedule_is_a_bijection(m_tiles, n_tiles, G):
     """Every workgroup tile of a launch is computed exactly once, whatever the grid."""
     n_gemm = m_tiles * n_tiles
-    for GM in (8, 4):  # the group heights the kernels use
+    for GM in (8, 4):  # the kernels' group height, and another
         seen = [_tile_of(item, n_gemm, G, m_tiles, n_tiles, GM) for item in range(n_gemm)]
         assert sorted(seen) == [(mi, ni) for mi in range(m_tiles) for ni in range(n_tiles)]
     # with the remap, the tiles one XCD holds in a round are a contiguous run of ids
