@@ -12,8 +12,12 @@ batch (inputs resident in HBM).  Prints one JSON line:
   cpu_baseline  the fp64 oracle timed on the host cores on a token slice of the
              same workload
 
-Default workload: the Llama-3-8B-like head (T=16384, H=4096, V=128256, bf16,
-about 45% of tokens active).
+Default workload: the stress head at its 50% point (T=262144, H=7168, V=129280,
+bf16), the largest workload that fits one GPU; --config 2 runs the Llama-3-8B-like
+head (T=16384, H=4096, V=128256, about 45% of tokens active).  The line also carries
+the median and minimum step time, the algorithmic bandwidth of the memory-bound
+kernels, device clocks before and after, a SHA-256 of the input bytes, and a
+secondary measurement of the tiny fp32 workload against the fp32 matrix peak.
 """
 
 from __future__ import annotations
@@ -40,8 +44,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=2)
-    p.add_argument("--active-frac", type=float, default=None, help="stress workload point")
+    p.add_argument("--config", type=int, default=5)
+    p.add_argument("--active-frac", type=float, default=None,
+                   help="stress workload point (default: its headline 50%%)")
+    p.add_argument("--no-hash", action="store_true", help="skip the SHA-256 of the input bytes")
+    p.add_argument("--no-secondary", action="store_true", help="skip the tiny fp32 secondary line")
     p.add_argument("--dense", action="store_true", help="dense fallback (no metadata)")
     p.add_argument("--cpu-tokens", type=int, default=1024, help="oracle slice (0 = skip)")
     p.add_argument("--no-trace", action="store_true")
@@ -145,6 +152,73 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def workload_label(cfg, frac):
+    """Name of a workload point: the config name, plus the active fraction for the
+    stress workload (whose points differ only in the mask)."""
+    return cfg.name if cfg.cid != 5 else f"{cfg.name} active={frac:.2f}"
+
+
+def clock_snapshot():
+    """Current and maximum engine/memory clocks and the power cap of the GPU, read with
+    rocm-smi (best effort: None fields where the tool or a field is unavailable)."""
+    import shutil
+    import subprocess
+
+    out = {"sclk": None, "mclk": None, "power_cap_w": None, "source": "rocm-smi"}
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(exe):
+        out["source"] = "unavailable"
+        return out
+    try:
+        res = subprocess.run([exe, "--showclocks", "--showmaxpower", "--json"], capture_output=True,
+                             text=True, timeout=30)
+        d = json.loads(res.stdout[res.stdout.find("{"):])
+    except Exception as e:  # noqa: BLE001 -- reporting only
+        out["source"] = f"rocm-smi failed: {type(e).__name__}"
+        return out
+    card = d.get("card0") or next((v for k, v in d.items() if k.startswith("card")), {})
+    for k, v in card.items():
+        kl = k.lower()
+        if kl.startswith("sclk") and "speed" in kl:
+            out["sclk"] = v
+        elif kl.startswith("mclk") and "speed" in kl:
+            out["mclk"] = v
+        elif "power" in kl and ("max" in kl or "cap" in kl):
+            out["power_cap_w"] = v
+    return out
+
+
+def input_sha256(*tensors, chunk=1 << 28):
+    """SHA-256 over the raw bytes of device tensors, in order, copied to the host in
+    chunks."""
+    import torch
+
+    hsh = hashlib.sha256()
+    for t in tensors:
+        flat = t.contiguous().view(-1).view(torch.uint8) if t.dtype != torch.uint8 else t.contiguous().view(-1)
+        for i in range(0, flat.numel(), chunk):
+            hsh.update(flat[i:i + chunk].cpu().numpy().tobytes())
+    return hsh.hexdigest()
+
+
+def aux_bytes(name, T, H, V, esz, A, n_spans, n_splits, ld_wt, ld_t):
+    """Algorithmic bytes per launch of the memory-bound kernels (reads + writes)."""
+    n_tiles = -(-T // 128)
+    if name == "spans_build":
+        return T + 8 * n_spans + 4 * -(-n_tiles // 32) + 8
+    if name == "bwd_lists":
+        return 4 * -(-n_tiles // 32) + 8 * n_spans + 4 * n_tiles + 8 * (T // 32 + n_spans) + 4 * -(-T // 32)
+    if name == "fwd_target_logit":
+        return 2 * T * H * esz + 8 * T + 4 * T
+    if name == "fwd_combine":
+        return -(-V // 256) * T * 16 + 4 * T + 12 * T
+    if name == "dhidden_finalize":
+        return A * H * 4 + T * H * esz + T + 4 * -(-T // 32)
+    if name == "transpose":  # the W and h transposes of one backward, per launch on average
+        return ((V * H + n_splits * H * ld_wt) + (T * H + H * ld_t)) * esz / 2
+    return None
+
+
 def stored_traffic(kernel: str, workload: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -178,6 +252,45 @@ def cpu_baseline(h, W, y, mask, a, b, n_tok):
                       f"forward+backward, {dt:.2f} s"}
 
 
+def tiny_fp32_line(torch, dev, steps=50, warmup=5):
+    """The tiny fp32 workload (T=512, H=256, V=4096) timed like the headline: tokens/s
+    and the method's flops against the fp32 matrix peak (the bf16 peak does not apply)."""
+    from entropy_block_sparse_amd import flh_backward, flh_forward, flh_spans_build, flh_workspace_bytes
+    from workloads import get_config, make_mask, make_tensors, make_upstream
+
+    cfg = get_config(1)
+    T, H, V = cfg.T, cfg.H, cfg.V
+    mask_np, _ = make_mask(1)
+    h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
+    a_np, b_np = make_upstream(mask_np)
+    mask = torch.as_tensor(mask_np).to(dev)
+    g_lp, g_ent = torch.as_tensor(a_np).to(dev), torch.as_tensor(b_np).to(dev)
+    ws_f = torch.empty(flh_workspace_bytes(1, h.dtype, T, H, V), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(flh_workspace_bytes(2, h.dtype, T, H, V, cfg.vocab_split), dtype=torch.uint8, device=dev)
+
+    def step():
+        meta = flh_spans_build(mask)
+        lp, ent, lse = flh_forward(h, W, y, workspace=ws_f)
+        return flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, cfg.vocab_split, workspace=ws_b)
+
+    for _ in range(warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    T_at, T_sp, _ = method_work(flh_spans_build(mask), T)
+    F = 2.0 * H * V * (T + T_at + T_sp + T)
+    return {"workload": cfg.name, "dtype": "f32", "value": T / (ms * 1e-3), "unit": "tokens/s",
+            "ms_per_step": ms, "median_ms": float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])),
+            "steps": steps, "frac_fp32_matrix_peak": F / (ms * 1e-3) / PEAK_FP32_MATRIX,
+            "note": "launch-latency bound: about 1 GFLOP per pass"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -194,7 +307,8 @@ def main():
 
     cfg = get_config(args.config)
     dev = torch.device("cuda:0")
-    mask_np, minfo = make_mask(cfg.cid, active_frac=args.active_frac)
+    frac_req = args.active_frac if args.active_frac is not None else (cfg.target_active if cfg.cid == 5 else None)
+    mask_np, minfo = make_mask(cfg.cid, active_frac=frac_req)
     T, H, V, Ssplit = cfg.T, cfg.H, cfg.V, cfg.vocab_split
     h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
     a_np, b_np = make_upstream(mask_np)
@@ -225,24 +339,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    clocks_before = clock_snapshot()
     trace = not args.no_trace
     if trace:
         trace_begin(64 * args.steps + 64)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     recs = trace_end(64 * args.steps + 64) if trace else []
+    clocks_after = clock_snapshot()
 
     # ---- algorithmic work of the method ----
     T_at, T_sp, spans = method_work(flh_spans_build(mask), T)
     A = int(mask_np.sum())
     pass_flops = 2.0 * H * V
+    F_min = pass_flops * (2 * T + 2 * A)
     T_dw = T_at if (args.skip_dw and not args.dense) else T  # tokens the weight gradient covers
     T_fwd = T_at if (args.skip_fwd and not args.dense) else T  # tokens the forward covers
     F_method = pass_flops * (T_fwd + T_at + T_sp + T_dw) if not args.dense else pass_flops * 4 * T
@@ -264,16 +381,28 @@ def main():
         "dlogits": pass_flops * T_at / n_splits,
         "dhidden_spans": pass_flops * T_sp / n_splits,
     }
+    esz = 2 if cfg.dtype == "bf16" else 4
+    n_sp = -(-V // Ssplit)
+    w_max = min(V, Ssplit)
+    pad = lambda n: (-(-n // 64) * 64) + (64 if (-(-n // 64)) % 2 == 0 else 0)  # noqa: E731
+    for k, d in per_kernel.items():
+        nb = aux_bytes(k, T, H, V, esz, A, len(spans), n_sp, pad(w_max), pad(-(-T // 128) * 128))
+        if nb is not None and d["ms_per_launch"] > 0:
+            d["alg_bytes_per_launch"] = nb
+            d["gbps"] = nb / (d["ms_per_launch"] * 1e-3) / 1e9
     roof = None
     if per_kernel:
         dom = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k]["ms"])
         achieved = alg[dom] / (per_kernel[dom]["ms_per_launch"] * 1e-3)
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": stored_traffic(dom, cfg.name)}
+                "traffic": stored_traffic(dom, workload_label(cfg, frac_req or 0.0))}
         for k in per_kernel:
             if k in alg:
                 per_kernel[k]["tflops"] = alg[k] / (per_kernel[k]["ms_per_launch"] * 1e-3) / 1e12
+
+    sha = None if args.no_hash else input_sha256(h, W, y, mask)
+    secondary = None if (args.no_secondary or cfg.cid == 1) else tiny_fp32_line(torch, dev)
 
     cpu = None
     if args.cpu_tokens > 0:
@@ -292,13 +421,21 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "T": T, "H": H, "V": V, "vocab_split": Ssplit,
+        "config": {"workload": workload_label(cfg, frac_req or 0.0), "T": T, "H": H, "V": V, "vocab_split": Ssplit,
                    "active_frac": minfo["active_frac"], "mask_seed": minfo["seed"],
                    "dense_fallback": bool(args.dense), "skip_inactive_dw": bool(args.skip_dw),
                    "skip_inactive_fwd": bool(args.skip_fwd), "padded_tail": bool(args.padded_tail)},
         "pct_peak_method": F_method / (ms * 1e-3) / peak,
+        "step_ms": {"mean": ms, "median": float(np.median(step_ms)), "min": float(np.min(step_ms)),
+                    "max": float(np.max(step_ms))},
+        "active_tokens_per_s": A / (ms * 1e-3),
         "work": {"A": A, "T_at128": int(T_at), "T_sp": int(T_sp), "spans": len(spans),
-                 "F_method_tflop": F_method / 1e12, "F_dense_tflop": 4 * pass_flops * T / 1e12},
+                 "F_method_tflop": F_method / 1e12, "F_min_tflop": F_min / 1e12,
+                 "F_dense_tflop": 4 * pass_flops * T / 1e12,
+                 "pct_peak_min": F_min / (ms * 1e-3) / peak},
+        "inputs": {"seed": cfg.seed, "mask_seed": minfo["seed"], "sha256_h_W_y_mask": sha},
+        "clocks": {"before": clocks_before, "after": clocks_after},
+        "secondary": secondary,
         "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": cpu,

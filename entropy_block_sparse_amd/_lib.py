@@ -10,7 +10,9 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflh.so")
+# FLH_LIBRARY names another build of the same ABI (the host-sanitizer build the ABI
+# tests load); by default the in-tree library.
+LIB_PATH = os.environ.get("FLH_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflh.so")
 
 FLH_OK = 0
 STATUS_NAMES = {

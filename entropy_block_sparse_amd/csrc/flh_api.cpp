@@ -28,12 +28,13 @@ enum KernelId : int32_t {
   kIdFinalize,
   kIdTranspose,
   kIdFwdLists,
+  kIdFwdTarget,
   kIdCount
 };
 const char *const kKernelNames[kIdCount] = {
     "spans_build", "fwd_logits_softmax", "fwd_combine", "bwd_lists",
     "dlogits",     "dhidden_spans",      "dweight",     "dhidden_finalize",
-    "transpose",   "fwd_lists"};
+    "transpose",   "fwd_lists",          "fwd_target_logit"};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -70,11 +71,11 @@ size_t fwd_bytes(int64_t T, int64_t V) {
 }
 
 struct BwdLayout {
-  size_t counts, tile_list, span_tiles, D, Dt, Wt, ht, acc, total;
+  size_t counts, tile_list, span_tiles, covered, D, Dt, Wt, ht, acc, total;
   int64_t span_tile_cap, ld_wt, ld_t;
 };
 
-// Backward workspace: [counts | token-tile list | span-tile list | d-logits
+// Backward workspace: [counts | token-tile list | span-tile list | covered-token bits | d-logits
 // staging [T][ld] sized by the widest live split | the same transposed, [W][ld_t] |
 // W^T per split [splits][H][ld_wt] | h^T [H][ld_t] | fp32 dH accumulator].  The transposed copies put
 // the contraction index of the hidden- and weight-gradient products in contiguous
@@ -97,6 +98,8 @@ BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   off = align_up(off + (size_t)n_skip * 4, 256);
   L.span_tiles = off;
   off = align_up(off + (size_t)L.span_tile_cap * 8, 256);
+  L.covered = off;
+  off = align_up(off + (size_t)cdiv(T, 32) * 4, 256);
   L.D = off;
   off = align_up(off + (size_t)T * (size_t)ld_max * esz, 256);
   L.Dt = off;
@@ -159,6 +162,23 @@ flh_status run(int32_t kid, int32_t split, hipStream_t st, F &&f) {
 }
 
 }  // namespace
+
+// Every check of a forward call except those of the workspace.
+flh_status flh::forward_check(flh_dtype dt, const void *h, const void *W, const int64_t *targets, int64_t T,
+                              int64_t H, int64_t V, const float *logprob, const float *entropy,
+                              const float *lse, const flh_active_meta *meta, uint32_t flags) {
+  if (!dtype_ok(dt)) return FLH_E_DTYPE;
+  if (flags & ~(uint32_t)FLH_FWD_SKIP_INACTIVE) return FLH_E_UNSUPPORTED;
+  if (!h || !W || !targets || !logprob || !entropy || !lse) return FLH_E_NULL;
+  if (!dims_ok(dt, T, H, V)) return FLH_E_SHAPE;
+  if (flags & FLH_FWD_SKIP_INACTIVE) {
+    if (!meta) return FLH_E_META;
+    if (!meta->tile_bits) return FLH_E_NULL;
+    if (meta->T != T || meta->tile_m != flh_tile_m(dt)) return FLH_E_META;
+  }
+  if (!aligned(h, 16) || !aligned(W, 16)) return FLH_E_ALIGN;
+  return FLH_OK;
+}
 
 extern "C" {
 
@@ -227,17 +247,11 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
                           int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
                           const flh_active_meta *meta, void *ws, size_t ws_bytes, void *stream,
                           uint32_t flags) {
-  if (!dtype_ok(dt)) return FLH_E_DTYPE;
-  if (flags & ~(uint32_t)FLH_FWD_SKIP_INACTIVE) return FLH_E_UNSUPPORTED;
+  const flh_status chk = flh::forward_check(dt, h, W, targets, T, H, V, logprob, entropy, lse, meta, flags);
+  if (chk != FLH_OK) return chk;
   const bool skip = (flags & FLH_FWD_SKIP_INACTIVE) != 0;
-  if (!h || !W || !targets || !logprob || !entropy || !lse || !ws) return FLH_E_NULL;
-  if (!dims_ok(dt, T, H, V)) return FLH_E_SHAPE;
-  if (skip) {
-    if (!meta) return FLH_E_META;
-    if (!meta->tile_bits) return FLH_E_NULL;
-    if (meta->T != T || meta->tile_m != flh_tile_m(dt)) return FLH_E_META;
-  }
-  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(ws, 256)) return FLH_E_ALIGN;
+  if (!ws) return FLH_E_NULL;
+  if (!aligned(ws, 256)) return FLH_E_ALIGN;
   if (ws_bytes < fwd_bytes(T, V)) return FLH_E_WORKSPACE;
   const int cus = num_cus();
   if (cus <= 0) return FLH_E_HIP;
@@ -270,9 +284,13 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
     s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwd, a, grid, st); });
   }
   if (s != FLH_OK) return s;
+  const uint32_t *skip_bits = skip ? meta->tile_bits : nullptr;
+  s = run(kIdFwdTarget, -1, st, [&] {
+    return launch_target_logit((int)dt, T, H, V, h, W, targets, logprob, st, skip_bits);
+  });
+  if (s != FLH_OK) return s;
   return run(kIdFwdCombine, -1, st, [&] {
-    return launch_combine((int)dt, T, H, V, h, W, a.part, targets, logprob, entropy, lse, st,
-                          skip ? meta->tile_bits : nullptr);
+    return launch_combine(T, V, a.part, logprob, entropy, lse, st, skip_bits);
   });
 }
 
@@ -303,7 +321,11 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
   if (meta) {
     if (!loss_mask) return FLH_E_META;
     if (!meta->spans || !meta->num_spans || !meta->tile_bits) return FLH_E_NULL;
-    if (meta->T != T || meta->tile_m != flh_tile_m(dt) || meta->span_cap < 0) return FLH_E_META;
+    // the span list must be able to hold every span this mask can have, as in
+    // flh_spans_build: a smaller capacity would have dropped spans
+    if (meta->T != T || meta->tile_m != flh_tile_m(dt) || meta->max_gap < 0 ||
+        meta->span_cap < flh_span_capacity(T, meta->max_gap))
+      return FLH_E_META;
   }
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(d_hidden, 16) || !aligned(d_weight, 16) ||
       !aligned(ws, 256))
@@ -347,7 +369,8 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
                         meta ? meta->num_spans : nullptr, meta ? meta->span_cap : 0,
                         reinterpret_cast<int32_t *>(base + L.tile_list),
                         reinterpret_cast<int32_t *>(base + L.counts),
-                        reinterpret_cast<int32_t *>(base + L.span_tiles), L.span_tile_cap, st);
+                        reinterpret_cast<int32_t *>(base + L.span_tiles), L.span_tile_cap, st,
+                        meta ? reinterpret_cast<uint32_t *>(base + L.covered) : nullptr);
   });
   if (s != FLH_OK) return s;
   s = run(kIdTranspose, -1, st, [&] {
@@ -394,7 +417,8 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
     if (s != FLH_OK) return s;
   }
   return run(kIdFinalize, -1, st, [&] {
-    return launch_finalize((int)dt, T, H, a.dh_acc, loss_mask, d_hidden, st);
+    return launch_finalize((int)dt, T, H, a.dh_acc, loss_mask,
+                           meta ? reinterpret_cast<const uint32_t *>(base + L.covered) : nullptr, d_hidden, st);
   });
 }
 
@@ -405,7 +429,7 @@ flh_status flh_trace_begin(int32_t capacity) {
   for (auto &e : tr.ev)
     if (hipEventCreate(&e) != hipSuccess) {
       for (auto &x : tr.ev)
-        if (x) hipEventDestroy(x);
+        if (x) (void)hipEventDestroy(x);
       tr.ev.clear();
       return FLH_E_HIP;
     }
@@ -429,7 +453,7 @@ int32_t flh_trace_end(flh_trace_record *records, int32_t max_records) {
       err = true;
     if (records && i < max_records) records[i] = flh_trace_record{tr.kid[i], tr.split[i], ms};
   }
-  for (auto &e : tr.ev) hipEventDestroy(e);
+  for (auto &e : tr.ev) (void)hipEventDestroy(e);
   tr.ev.clear();
   tr.on = false;
   tr.n = 0;

@@ -8,7 +8,8 @@
 //            ones first, so d-logits workgroups pair up active tiles) and
 //            span-local row tiles for the hidden-gradient projection.
 //   combine  per-tile softmax states -> logprob, entropy, lse per token.
-//   finalize fp32 hidden-gradient accumulator -> output dtype, inactive rows +0.
+//   finalize fp32 hidden-gradient accumulator -> output dtype, inactive rows +0,
+//            NaN rows for active tokens the metadata does not cover.
 //
 // spans and lists run as one workgroup of 1024 threads: the mask is at most a
 // few hundred KiB, so a single pass through L2 is far cheaper than a multi-kernel
@@ -154,7 +155,8 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
                                                        int64_t span_cap, int32_t *__restrict__ tile_list,
                                                        int32_t *__restrict__ counts,
                                                        int32_t *__restrict__ span_tiles,
-                                                       int64_t span_tile_cap) {
+                                                       int64_t span_tile_cap,
+                                                       uint32_t *__restrict__ covered) {
   __shared__ int64_t sh[kBlock];
   const int tid = threadIdx.x;
   const int64_t n_tiles = (T + kSkipTile - 1) / kSkipTile;
@@ -190,22 +192,62 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
     run_i += tot_i;
   }
 
-  // span pieces of at most kSpanPiece rows, starting at each span start (span order)
+  // Spans as the kernels use them: the count clamped to [0, span_cap] and every span
+  // to 0 <= start <= end <= T, so that metadata that does not belong to this call
+  // (built from another mask, or never built) cannot send a launch outside its rows.
   int64_t ns = spans ? (int64_t)(*num_spans) : 1;
-  if (spans && ns > span_cap) ns = span_cap;
+  if (ns > span_cap && spans) ns = span_cap;
+  if (ns < 0) ns = 0;
+  auto span_at = [&](int64_t k, int64_t &s, int64_t &e) {
+    if (!spans) {
+      s = 0;
+      e = T;
+      return;
+    }
+    s = spans[2 * k];
+    e = spans[2 * k + 1];
+    s = s < 0 ? 0 : (s > T ? T : s);
+    e = e < s ? s : (e > T ? T : e);
+  };
+
+  // Tokens the metadata covers, one bit per token: inside a span and in a token tile
+  // whose bit is set.  With metadata built from this call's mask every active token is
+  // covered; the finalize step gives an active token that is not a NaN hidden-gradient
+  // row, so inconsistent metadata fails loudly instead of leaving stale or zero rows.
+  if (covered) {
+    const int64_t n_cw = (T + 31) / 32;
+    for (int64_t w = tid; w < n_cw; w += kBlock) {
+      const int64_t t0 = w * 32;
+      int64_t lo = 0, hi = ns;  // first span whose end is past t0 (ends ascend)
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        int64_t s, e;
+        span_at(mid, s, e);
+        if (e <= t0) lo = mid + 1;
+        else hi = mid;
+      }
+      int64_t k = lo, ks = 0, ke = 0;
+      if (k < ns) span_at(k, ks, ke);
+      uint32_t word = 0u;
+      for (int b = 0; b < 32 && t0 + b < T; ++b) {
+        const int64_t t = t0 + b;
+        while (k < ns && ke <= t) {
+          ++k;
+          if (k < ns) span_at(k, ks, ke);
+        }
+        const bool in_span = k < ns && ks <= t;
+        if (in_span && active(t / kSkipTile)) word |= 1u << b;
+      }
+      covered[w] = word;
+    }
+  }
+
+  // span pieces of at most kSpanPiece rows, starting at each span start (span order)
   int64_t run = 0;
   for (int64_t base = 0; base < ns; base += kBlock) {
     const int64_t k = base + tid;
     int64_t s = 0, e = 0;
-    if (k < ns) {
-      if (spans) {
-        s = spans[2 * k];
-        e = spans[2 * k + 1];
-      } else {
-        s = 0;
-        e = T;
-      }
-    }
+    if (k < ns) span_at(k, s, e);
     const int64_t ntl = (e > s) ? (e - s + kSpanPiece - 1) / kSpanPiece : 0;
     const int64_t incl = block_scan(ntl, sh, AddOp());
     const int64_t tot = sh[kBlock - 1];
@@ -341,9 +383,12 @@ __global__ __launch_bounds__(256) void target_logit_kernel(int64_t T, int64_t H,
   if (lane == 0) out[t] = acc;
 }
 
+// covered: NULL (every token's row was accumulated), or the bitmap of tokens the
+// active metadata covers; an active token outside it gets a NaN row.
 template <typename T>
 __global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, const float *__restrict__ acc,
                                                        const uint8_t *__restrict__ mask,
+                                                       const uint32_t *__restrict__ covered,
                                                        T *__restrict__ dh) {
   constexpr int kPer = 16 / sizeof(T);
   const int64_t per_row = H / kPer;
@@ -353,6 +398,14 @@ __global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, co
     const int64_t t = idx / per_row;
     const int64_t c = (idx - t * per_row) * kPer;
     const bool act = mask ? (mask[t] != 0) : true;
+    if (act && covered && !((covered[t >> 5] >> (t & 31)) & 1u)) {
+      // an active token the metadata does not cover: its accumulator row was never written
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint4 *>(dh + t * H + c) = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+      else
+        *reinterpret_cast<uint4 *>(dh + t * H + c) = make_uint4(0x7fc00000u, 0x7fc00000u, 0x7fc00000u, 0x7fc00000u);
+      continue;
+    }
     if constexpr (sizeof(T) == 2) {
       uint32_t w[4] = {0u, 0u, 0u, 0u};
       if (act) {
@@ -390,15 +443,16 @@ hipError_t launch_spans(const uint8_t *mask, int64_t T, int32_t max_gap, int32_t
 
 hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spans,
                         const int32_t *num_spans, int64_t span_cap, int32_t *tile_list,
-                        int32_t *counts, int32_t *span_tiles, int64_t span_tile_cap, hipStream_t st) {
+                        int32_t *counts, int32_t *span_tiles, int64_t span_tile_cap, hipStream_t st,
+                        uint32_t *covered) {
   hipLaunchKernelGGL(lists_kernel, dim3(1), dim3(kBlock), 0, st, T, tile_bits, spans, num_spans,
-                     span_cap, tile_list, counts, span_tiles, span_tile_cap);
+                     span_cap, tile_list, counts, span_tiles, span_tile_cap, covered);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
-                          const float *part, const int64_t *targets, float *logprob, float *entropy,
-                          float *lse, hipStream_t st, const uint32_t *skip_bits) {
+hipError_t launch_target_logit(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
+                               const int64_t *targets, float *logprob, hipStream_t st,
+                               const uint32_t *skip_bits) {
   const unsigned tl_blocks = (unsigned)((T + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(target_logit_kernel<uint16_t>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
@@ -408,8 +462,11 @@ hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void
     hipLaunchKernelGGL(target_logit_kernel<float>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
                        reinterpret_cast<const float *>(h), reinterpret_cast<const float *>(W), targets,
                        skip_bits, logprob);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int64_t T, int64_t V, const float *part, float *logprob, float *entropy,
+                          float *lse, hipStream_t st, const uint32_t *skip_bits) {
   const int64_t blocks = (T + 63) / 64;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(64 * kCombWaves), 0, st, T, V,
                      reinterpret_cast<const float4 *>(part), skip_bits, logprob, entropy, lse);
@@ -417,7 +474,7 @@ hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void
 }
 
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, const uint8_t *mask,
-                           void *dh, hipStream_t st) {
+                           const uint32_t *covered, void *dh, hipStream_t st) {
   const int64_t per = dtype == 1 ? 8 : 4;
   const int64_t n = T * (H / per);
   int64_t blocks = (n + 255) / 256;
@@ -425,10 +482,10 @@ hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, co
   if (blocks < 1) blocks = 1;
   if (dtype == 1)
     hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, T, H, acc,
-                       mask, reinterpret_cast<uint16_t *>(dh));
+                       mask, covered, reinterpret_cast<uint16_t *>(dh));
   else
     hipLaunchKernelGGL(finalize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, T, H, acc,
-                       mask, reinterpret_cast<float *>(dh));
+                       mask, covered, reinterpret_cast<float *>(dh));
   return hipGetLastError();
 }
 

@@ -5,7 +5,15 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "flh.h"
+
 namespace flh {
+
+// Argument checks of a forward call (flh_forward_ex), all but the workspace's.
+flh_status forward_check(flh_dtype dt, const void *h, const void *W, const int64_t *targets, int64_t T,
+                         int64_t H, int64_t V, const float *logprob, const float *entropy, const float *lse,
+                         const flh_active_meta *meta, uint32_t flags);
+
 
 // Macro tile of every contraction: 256 x 256 outputs per workgroup, 4 waves of
 // 128 x 128, K staged 128 bytes at a time (64 bf16 or 32 fp32).
@@ -84,17 +92,24 @@ hipError_t launch_spans(const uint8_t *mask, int64_t T, int32_t max_gap, int32_t
                         int64_t span_cap, int32_t *spans, int32_t *num_spans,
                         uint32_t *tile_bits, int32_t *active_count, hipStream_t st);
 
+// Work lists of the backward (and of the forward over active tiles: spans NULL, no
+// pieces).  Spans are read with their count clamped to [0, span_cap] and each span to
+// [0, T].  covered (optional, [ceil(T/32)] words): bit t set iff token t lies inside a
+// span and in a token tile whose bit is set.
 hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spans,
                         const int32_t *num_spans, int64_t span_cap, int32_t *tile_list,
                         int32_t *counts, int32_t *span_tiles, int64_t span_tile_cap,
-                        hipStream_t st);
+                        hipStream_t st, uint32_t *covered = nullptr);
 
-// Target logits z_y = h[t] . W[y_t] into logprob, then the merge of the per-tile
-// softmax states into lse, entropy and logprob = z_y - lse.
+// Target logits z_y = h[t] . W[y_t] into logprob (NaN for a target outside [0, V)).
 // skip_bits: NULL, or the tile bitmap of a forward over active token tiles only (the
-// other tiles' tokens get 0 for all three outputs).
-hipError_t launch_combine(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
-                          const float *part, const int64_t *targets, float *logprob, float *entropy,
+// other tiles' tokens are left alone).
+hipError_t launch_target_logit(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
+                               const int64_t *targets, float *logprob, hipStream_t st,
+                               const uint32_t *skip_bits = nullptr);
+// The merge of the per-tile softmax states into lse, entropy and logprob = z_y - lse
+// (logprob holds z_y on entry).  skip_bits as above; skipped tokens get 0 for all three.
+hipError_t launch_combine(int64_t T, int64_t V, const float *part, float *logprob, float *entropy,
                           float *lse, hipStream_t st, const uint32_t *skip_bits = nullptr);
 
 // Blocked transpose: rows of `in` ([R][C] row-major, elements of esz bytes, 2 or 4)
@@ -109,7 +124,9 @@ hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void 
                             int64_t block, hipStream_t st, const int32_t *row_tiles = nullptr,
                             const int32_t *n_row_tiles = nullptr);
 
+// dh = acc rounded to the output dtype for active tokens, +0 for inactive ones, NaN
+// for active tokens outside `covered` (NULL: every token covered).
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc,
-                           const uint8_t *mask, void *dh, hipStream_t st);
+                           const uint8_t *mask, const uint32_t *covered, void *dh, hipStream_t st);
 
 }  // namespace flh

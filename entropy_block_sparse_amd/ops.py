@@ -123,6 +123,28 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
 
 
+def _check_operands(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor):
+    """(T, H, V) of a call, after the checks the C ABI cannot make from plain pointers:
+    the kernels would read past a tensor that is shorter than the sizes say."""
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError(f"h and W must be 2-D, got {tuple(h.shape)} and {tuple(W.shape)}")
+    if h.dtype != W.dtype:
+        raise TypeError(f"h and W must share a dtype, got {h.dtype} and {W.dtype}")
+    _dtype_code(h)
+    T, H = h.shape
+    V = W.shape[0]
+    if W.shape[1] != H:
+        raise ValueError(f"W has {W.shape[1]} columns, h has {H}")
+    if targets.numel() != T:
+        raise ValueError(f"targets has {targets.numel()} elements, h has {T} rows")
+    return int(T), int(H), int(V)
+
+
+def _check_len(name: str, t: Optional[torch.Tensor], T: int) -> None:
+    if t is not None and t.numel() != T:
+        raise ValueError(f"{name} has {t.numel()} elements, expected one per token ({T})")
+
+
 def flh_forward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                 workspace: Optional[torch.Tensor] = None, meta: Optional["ActiveMetaTensors"] = None,
                 skip_inactive: bool = False):
@@ -130,15 +152,10 @@ def flh_forward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
 
     skip_inactive: flh_forward_ex's FLH_FWD_SKIP_INACTIVE (needs meta): the forward over
     active 128-token tiles only; the other tiles' tokens get 0."""
+    T, H, V = _check_operands(h, W, targets)
     _require_cuda(h, W, targets)
-    if h.dtype != W.dtype:
-        raise TypeError("h and W must share a dtype")
     h, W = h.contiguous(), W.contiguous()
     targets = targets.to(torch.int64).contiguous()
-    T, H = h.shape
-    V = W.shape[0]
-    if W.shape[1] != H or targets.numel() != T:
-        raise ValueError("shape mismatch")
     dev = h.device
     lp = torch.empty(T, dtype=torch.float32, device=dev)
     ent = torch.empty(T, dtype=torch.float32, device=dev)
@@ -169,14 +186,23 @@ def flh_backward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
     over active token tiles only; same result).
     padded_tail: FLH_BWD_PADDED_TAIL, the padded-staging baseline of the live-width split
     (a measurement probe; same result)."""
+    T, H, V = _check_operands(h, W, targets)
+    for name, t in (("lse", lse), ("entropy", entropy), ("grad_logprob", grad_logprob),
+                    ("grad_entropy", grad_entropy), ("loss_mask", loss_mask)):
+        _check_len(name, t, T)
+    if lse is None or entropy is None:
+        raise ValueError("lse and entropy saved by flh_forward are required")
+    if meta is not None:
+        if loss_mask is None:
+            raise ValueError("active metadata needs the loss mask it was built from")
+        if meta.T != T:
+            raise ValueError(f"active metadata describes {meta.T} tokens, the call has {T}")
     _require_cuda(h, W, targets, lse, entropy, grad_logprob, grad_entropy, loss_mask)
     h, W = h.contiguous(), W.contiguous()
     targets = targets.to(torch.int64).contiguous()
     lse, entropy = _f32(lse), _f32(entropy)
     g_lp, g_ent = _f32(grad_logprob), _f32(grad_entropy)
     m = _mask_u8(loss_mask)
-    T, H = h.shape
-    V = W.shape[0]
     dev = h.device
     dH = torch.empty((T, H), dtype=h.dtype, device=dev)
     dW = torch.empty((V, H), dtype=h.dtype, device=dev)

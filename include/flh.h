@@ -44,7 +44,11 @@
  *     exception crosses the ABI.
  *   - Not checked (that would need a device read): targets in [0, V) (a target
  *     out of range gives logprob = NaN for that token), finite inputs, and that
- *     `meta` was built from the same loss mask.
+ *     `meta` was built from the same loss mask.  flh_backward reads the metadata's
+ *     spans clamped to [0, T] (and their count to span_cap), so metadata of another
+ *     mask never sends a launch outside its buffers, and an active token that such
+ *     metadata leaves out (outside every span, or in a tile whose bit is clear) gets a
+ *     NaN d_hidden row rather than a silently wrong or zero one.
  *   - Results are bit-identical from run to run (no floating-point atomics).
  *   - Calls on different streams may run concurrently if their buffers differ.
  */
@@ -60,7 +64,16 @@ extern "C" {
 
 #define FLH_ABI_VERSION 1
 
-typedef enum {
+/* The enums below are int-sized in C; compiled as C++ they get `int` as their fixed
+ * underlying type, so that any value a C caller passes (an unknown dtype, say) is a
+ * valid value of the type and is rejected by the checks rather than being undefined. */
+#ifdef __cplusplus
+#define FLH_ENUM_INT : int
+#else
+#define FLH_ENUM_INT
+#endif
+
+typedef enum FLH_ENUM_INT {
   FLH_OK = 0,
   FLH_E_NULL = 1,        /* a required pointer is NULL                               */
   FLH_E_SHAPE = 2,       /* a size is <= 0, too large, or not a supported multiple   */
@@ -72,10 +85,10 @@ typedef enum {
   FLH_E_HIP = 8          /* a HIP runtime call or kernel launch failed               */
 } flh_status;
 
-typedef enum { FLH_F32 = 0, FLH_BF16 = 1 } flh_dtype;
+typedef enum FLH_ENUM_INT { FLH_F32 = 0, FLH_BF16 = 1 } flh_dtype;
 
 /* Which call a workspace size is for. */
-typedef enum { FLH_OP_SPANS = 0, FLH_OP_FORWARD = 1, FLH_OP_BACKWARD = 2 } flh_op;
+typedef enum FLH_ENUM_INT { FLH_OP_SPANS = 0, FLH_OP_FORWARD = 1, FLH_OP_BACKWARD = 2 } flh_op;
 
 /*
  * Active metadata derived from the loss mask (SkyRL #2376, "How it works": one
@@ -123,7 +136,7 @@ int64_t flh_span_capacity(int64_t T, int32_t max_gap);
  * vocab_split 0 means 16384.  Returns 0 for invalid sizes as well.
  * Forward: per-tile softmax partials, ceil(V/256) * T * 16 bytes, and the active
  * token-tile list (4 * ceil(T/128) bytes plus alignment).
- * Backward: work lists; the d-logits staging of the widest split in two layouts
+ * Backward: work lists and a token bitmap; the d-logits staging of the widest split in two layouts
  * (token-major T x W and vocabulary-major W x T, W = min(V, vocab_split)); W and h
  * transposed (H x V and H x T, so that every contraction reads its contraction
  * index contiguously); and an fp32 T x H hidden-gradient accumulator.  For
@@ -190,8 +203,11 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
  *                  when no spans are provided).  Otherwise metadata built from
  *                  `loss_mask` by flh_spans_build: d-logits tiles without an active
  *                  token are skipped and d_hidden is projected over the spans only
- *                  ("How it works").  Requires loss_mask != NULL, meta->T == T and
- *                  meta->tile_m == flh_tile_m(dt), else FLH_E_META.
+ *                  ("How it works").  Requires loss_mask != NULL, meta->T == T,
+ *                  meta->tile_m == flh_tile_m(dt), meta->max_gap >= 0 and
+ *                  meta->span_cap >= flh_span_capacity(T, meta->max_gap), else
+ *                  FLH_E_META (a smaller span list could have dropped spans, whose
+ *                  tokens would then get no gradient: Bugbot "Note").
  *   vocab_split    split width S (0 = 16384), a multiple of 256.  Split s covers
  *                  vocabulary rows [s*S, s*S + W_s) with W_s = min(S, V - s*S); its
  *                  d-logits staging buffer and every launch over it are sized by

@@ -135,6 +135,13 @@ def test_backward_validation():
     assert _bwd(meta=_meta(T=511)) == E["FLH_E_META"]
     assert _bwd(meta=_meta(T=512, tm=64)) == E["FLH_E_META"]
     assert _bwd(meta=_meta(T=512, spans=None)) == E["FLH_E_NULL"]
+    # a span list that cannot hold every span of this T would have dropped spans, and a
+    # negative gap is no metadata flh_spans_build can build (Bugbot "Note": wrong spans
+    # silently zero gradients)
+    assert _bwd(meta=_meta(T=512, G=-1, cap=512)) == E["FLH_E_META"]
+    assert _bwd(meta=_meta(T=512, G=0, cap=255)) == E["FLH_E_META"]      # needs 256
+    assert _bwd(meta=_meta(T=512, G=128, cap=3)) == E["FLH_E_META"]     # needs 4
+    assert _bwd(meta=_meta(T=512, G=128, cap=-1)) == E["FLH_E_META"]
     assert _bwd(dH=FAKE_ODD) == E["FLH_E_ALIGN"]
     assert _bwd(dW=FAKE_ODD) == E["FLH_E_ALIGN"]
     assert _bwd(nbytes=1000) == E["FLH_E_WORKSPACE"]
@@ -182,3 +189,4 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 src = open(os.path.join(root, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
+

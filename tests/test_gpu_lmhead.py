@@ -24,6 +24,20 @@ pytestmark = pytest.mark.gpu
 
 TOL_LP = 5e-3
 TOL_GRAD = 1e-2
+TOL_TILE = 2e-2
+
+
+def tile_rel_fro(got, ref, tile=256):
+    """Largest relative Frobenius error over the tile x tile blocks whose reference is
+    not zero."""
+    worst = 0.0
+    for r in range(0, ref.shape[0], tile):
+        for c in range(0, ref.shape[1], tile):
+            o = ref[r:r + tile, c:c + tile]
+            den = np.linalg.norm(o)
+            if den > 0:
+                worst = max(worst, float(np.linalg.norm(got[r:r + tile, c:c + tile] - o) / den))
+    return worst
 
 
 def bursty_mask(T, seed, p_on=0.5, max_run=400):
@@ -65,6 +79,9 @@ def run_case(T, H, V, dtype, mask, mode="lp+ent", vocab_split=0, use_meta=True, 
     gdH, gdW = host64(dH), host64(dW)
     assert rel_fro(gdH, odH) <= TOL_GRAD, rel_fro(gdH, odH)
     assert rel_fro(gdW, odW) <= TOL_GRAD, rel_fro(gdW, odW)
+    # every 256 x 256 block of d_weight on its own (a lost or misplaced block fails)
+    if mode != "random":
+        assert tile_rel_fro(gdW, odW) <= TOL_TILE, tile_rel_fro(gdW, odW)
     inactive = mask == 0
     if inactive.any():
         raw = dH.view(torch.int16 if dtype == "bf16" else torch.int32).cpu().numpy()
@@ -237,6 +254,12 @@ def test_forward_skip_inactive_matches_dense(dtype, T, H, V, split, kind):
     for d, s in zip(dense, sparse):
         assert torch.equal(d[act_dev], s[act_dev])
         assert not s[~act_dev].any()
+    # and directly against the oracle: its values on tokens of active tiles, 0 elsewhere
+    olp, oent, olse = O.forward(host64(h), host64(W), y.cpu().numpy())
+    for got, ref in zip(sparse, (olp, oent, olse)):
+        g = got.cpu().numpy()
+        assert max_abs(g[in_active], ref[in_active]) <= TOL_LP
+        assert not g[~in_active].any()
     a, b = make_upstream(mask)
     g_lp, g_ent = torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev)
     ref = flh_backward(h, W, y, dense[2], dense[1], g_lp, g_ent, m, meta, split)
@@ -277,3 +300,67 @@ def test_padded_tail_probe_rejects_fp32():
     lp, ent, lse = flh_forward(h, W, y)
     with pytest.raises(FlhError):
         flh_backward(h, W, y, lse, ent, None, None, m, meta, 256, padded_tail=True)
+
+
+@pytest.mark.parametrize("masked,use_entropy", [(True, True), (True, False), (False, True)])
+def test_autograd_op_against_oracle(masked, use_entropy):
+    """fused_lm_head as a torch.autograd.Function (the analogue of the pages' op that
+    takes optional spans; Bugbot "Overview"): the loss sum_t (a_t logprob_t + b_t
+    entropy_t) differentiated through .backward() gives h.grad and W.grad equal to the
+    oracle's d_hidden and d_weight for upstream gradients a and b."""
+    from entropy_block_sparse_amd import fused_lm_head
+    dev = cuda_device()
+    T, H, V = 900, 200, 3100
+    announce(f"autograd T={T} H={H} V={V} masked={masked} entropy={use_entropy}")
+    mask = bursty_mask(T, 61) if masked else np.ones(T, np.uint8)
+    h0, W0, y = make_tensors(T, H, V, "bf16", 62)
+    h = h0.to(dev).requires_grad_(True)
+    W = W0.to(dev).requires_grad_(True)
+    y = y.to(dev)
+    a, b = make_upstream(mask, "random", seed=63)
+    lp, ent = fused_lm_head(h, W, y, torch.as_tensor(mask).to(dev) if masked else None, vocab_split=1024)
+    loss = (lp * torch.as_tensor(a).to(dev)).sum()
+    if use_entropy:
+        loss = loss + (ent * torch.as_tensor(b).to(dev)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    hh, WW, yy = host64(h0), host64(W0), y.cpu().numpy()
+    olp, oent, _ = O.forward(hh, WW, yy)
+    assert max_abs(lp.detach().cpu().numpy(), olp) <= TOL_LP
+    assert max_abs(ent.detach().cpu().numpy(), oent) <= TOL_LP
+    odH, odW = O.backward(hh, WW, yy, mask if masked else None, a, b if use_entropy else None)
+    assert h.grad.dtype == torch.bfloat16 and W.grad.dtype == torch.bfloat16
+    assert rel_fro(host64(h.grad), odH) <= TOL_GRAD
+    assert rel_fro(host64(W.grad), odW) <= TOL_GRAD
+    assert tile_rel_fro(host64(W.grad), odW) <= TOL_TILE
+    if masked:
+        assert not h.grad.view(torch.int16).cpu().numpy()[mask == 0].any()
+
+
+def test_metadata_of_another_mask_gives_nan_rows_not_silent_ones():
+    """Metadata built from a different mask than the backward's: the rows of active
+    tokens it covers (inside one of its spans and its active tiles) are still right, the
+    active tokens it leaves out get NaN rows instead of stale or zero ones, and inactive
+    rows stay +0 (Bugbot "Note": wrong spans would silently zero gradients)."""
+    dev = cuda_device()
+    T, H, V = 1000, 64, 1500
+    announce("metadata of another mask")
+    built = np.zeros(T, np.uint8)
+    built[0:400] = 1
+    used = np.zeros(T, np.uint8)
+    used[300:700] = 1
+    h, W, y = [x.to(dev) for x in make_tensors(T, H, V, "bf16", 71)]
+    a, b = make_upstream(used)
+    meta = flh_spans_build(torch.as_tensor(built).to(dev))
+    lp, ent, lse = flh_forward(h, W, y)
+    dH, _ = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                         torch.as_tensor(used).to(dev), meta, 512)
+    torch.cuda.synchronize()
+    g = host64(dH)
+    odH, _ = O.backward(host64(h), host64(W), y.cpu().numpy(), used, a, b)
+    covered = np.arange(300, 400)
+    assert np.isfinite(g[covered]).all()
+    assert rel_fro(g[covered], odH[covered]) <= TOL_GRAD
+    assert np.isnan(g[400:700]).all()
+    raw = dH.view(torch.int16).cpu().numpy()
+    assert not raw[used == 0].any()

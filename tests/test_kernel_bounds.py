@@ -568,3 +568,35 @@ def test_span_pieces_cover_spans_exactly(seed):
     for a, b in spans:
         inside[a:b] = 1
     assert (covered == inside).all()
+
+
+def clamped_spans(raw, num, span_cap, T):
+    """Host model of how the work-list kernel reads a span list it cannot trust: the
+    count clamped to [0, span_cap], each span to 0 <= start <= end <= T."""
+    ns = max(0, min(num, span_cap))
+    out = []
+    for k in range(ns):
+        s, e = raw[k]
+        s = min(max(s, 0), T)
+        e = min(max(e, s), T)
+        out.append((s, e))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_span_clamp_keeps_every_piece_inside_the_rows(seed):
+    """Metadata that does not belong to the call (another mask, garbage counts or
+    coordinates): the pieces the hidden-gradient launch reads and writes stay inside
+    [0, T), and at most span_tile_cap of them are stored."""
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 3000))
+    cap = int(rng.integers(0, 40))
+    raw = [(int(rng.integers(-5000, 8000)), int(rng.integers(-5000, 8000))) for _ in range(cap)]
+    num = int(rng.integers(-10, 80))
+    pieces = span_pieces(clamped_spans(raw, num, cap, T))
+    span_tile_cap = cdiv(T, PIECE) + (T + 1) // 2 + 1
+    stored = pieces[:span_tile_cap]
+    for r0, r1 in stored:
+        assert 0 <= r0 < r1 <= T and r1 - r0 <= PIECE
+    # the coverage bitmap has one bit per token; its words are indexed below ceil(T/32)
+    assert all(t >> 5 < cdiv(T, 32) for t in range(T))
