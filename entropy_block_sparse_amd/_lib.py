@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("FLH_LIBRARY") or os.path.join(os.path.dirname(os.path
 FLH_OK = 0
 STATUS_NAMES = {
     0: "FLH_OK", 1: "FLH_E_NULL", 2: "FLH_E_SHAPE", 3: "FLH_E_DTYPE", 4: "FLH_E_ALIGN",
-    5: "FLH_E_WORKSPACE", 6: "FLH_E_META", 7: "FLH_E_UNSUPPORTED", 8: "FLH_E_HIP",
+    5: "FLH_E_WORKSPACE", 6: "FLH_E_META", 7: "FLH_E_UNSUPPORTED", 8: "FLH_E_HIP", 9: "FLH_E_SCRATCH",
 }
 FLH_F32, FLH_BF16 = 0, 1
 OP_SPANS, OP_FORWARD, OP_BACKWARD = 0, 1, 2
@@ -65,6 +65,9 @@ SIGNATURES = [
     ("flh_forward_ex", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta), _VP, _SZ,
       _VP, ctypes.c_uint32]),
+    ("flh_forward_noalloc", ctypes.c_int,
+     [ctypes.c_int, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta), _VP,
+      ctypes.c_uint32]),
     ("flh_backward", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
       _I64, _I64, _I64, _I32, _VP, _VP, _VP, _SZ, _VP]),

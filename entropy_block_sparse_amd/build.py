@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflh.so")
 ARCH = "gfx950"
 
-SOURCES = ["flh_gemm.hip", "flh_aux.hip", "flh_api.cpp"]
+SOURCES = ["flh_gemm.hip", "flh_aux.hip", "flh_api.cpp", "flh_noalloc.hip"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -195,6 +195,7 @@ const char *flh_status_string(flh_status s) {
     case FLH_E_META: return "active metadata inconsistent with the call";
     case FLH_E_UNSUPPORTED: return "unsupported request";
     case FLH_E_HIP: return "HIP runtime error";
+    case FLH_E_SCRATCH: return "sizes exceed the library's static scratch (flh_forward_noalloc)";
   }
   return "unknown status";
 }

@@ -82,7 +82,8 @@ typedef enum FLH_ENUM_INT {
   FLH_E_WORKSPACE = 5,   /* ws_bytes smaller than flh_workspace_bytes()              */
   FLH_E_META = 6,        /* active metadata inconsistent with this call              */
   FLH_E_UNSUPPORTED = 7, /* valid request the library does not support               */
-  FLH_E_HIP = 8          /* a HIP runtime call or kernel launch failed               */
+  FLH_E_HIP = 8,         /* a HIP runtime call or kernel launch failed               */
+  FLH_E_SCRATCH = 9      /* sizes exceed the static scratch (flh_forward_noalloc)   */
 } flh_status;
 
 typedef enum FLH_ENUM_INT { FLH_F32 = 0, FLH_BF16 = 1 } flh_dtype;
@@ -189,6 +190,28 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
                           int64_t T, int64_t H, int64_t V, float *logprob, float *entropy,
                           float *lse, const flh_active_meta *meta, void *ws, size_t ws_bytes,
                           void *stream, uint32_t flags);
+
+/*
+ * flh_forward_ex for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same call
+ * without a workspace argument.  Its scratch (the per-tile softmax states and the
+ * active-tile list) is a static device array of FLH_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU the library runs on, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no library routine that allocates); its address is
+ * looked up once per device, on the first call made with that device current.
+ *   Limit: flh_workspace_bytes(FLH_OP_FORWARD, dt, T, H, V, 0) must not exceed
+ *   FLH_NOALLOC_SCRATCH_BYTES (128 MiB: for V = 128256, up to T = 16743 tokens), else
+ *   FLH_E_SCRATCH and nothing is enqueued.  Other arguments and errors as for
+ *   flh_forward_ex.
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents (every byte a call reads was written earlier in the same call, so nothing
+ *   needs clearing): calls that may overlap on one GPU (other streams, other host
+ *   threads) race and must be serialised by the caller.
+ */
+#define FLH_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+flh_status flh_forward_noalloc(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                               int64_t T, int64_t H, int64_t V, float *logprob, float *entropy,
+                               float *lse, const flh_active_meta *meta, void *stream, uint32_t flags);
 
 /*
  * Backward: d_hidden [T,H] and d_weight [V,H] (dtype dt, both overwritten) from

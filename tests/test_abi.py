@@ -41,7 +41,7 @@ def test_abi_version_and_queries():
     assert L.flh_span_capacity(16384, 128) == 127
     assert L.flh_span_capacity(262144, 128) == 2017
     assert L.flh_span_capacity(0, 128) == 0 and L.flh_span_capacity(10, -1) == 0
-    for s in range(9):
+    for s in range(10):
         assert L.flh_status_string(s)
 
 
@@ -190,3 +190,26 @@ def test_product_path_does_not_import_oracle():
                 src = open(os.path.join(root, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
 
+
+def _fwd_na(dt=1, T=512, H=256, V=4096, flags=0, meta="ok", h=FAKE, lp=FAKE):
+    m = _meta(T=T) if meta == "ok" else meta
+    mp = ctypes.byref(m) if m is not None else None
+    return lib().flh_forward_noalloc(dt, h, FAKE, FAKE, T, H, V, lp, FAKE, FAKE, mp, None, flags)
+
+
+def test_noalloc_forward_validation():
+    """The no-allocation forward: the forward's own checks, and sizes whose workspace
+    would not fit the library's static scratch refused before anything runs."""
+    L = lib()
+    cap = 128 << 20
+    assert _fwd_na(dt=4) == E["FLH_E_DTYPE"]
+    assert _fwd_na(h=None) == E["FLH_E_NULL"] and _fwd_na(lp=None) == E["FLH_E_NULL"]
+    assert _fwd_na(H=12) == E["FLH_E_SHAPE"]
+    assert _fwd_na(flags=1 << 4) == E["FLH_E_UNSUPPORTED"]
+    assert _fwd_na(flags=1, meta=None) == E["FLH_E_META"]
+    assert _fwd_na(h=FAKE_ODD) == E["FLH_E_ALIGN"]
+    # at V = 128256 the Llama-3-8B-like head's T = 16384 fits; the largest T is 16743
+    assert L.flh_workspace_bytes(1, 1, 16743, 4096, 128256, 0) <= cap
+    assert L.flh_workspace_bytes(1, 1, 16744, 4096, 128256, 0) > cap
+    assert _fwd_na(T=16744, H=4096, V=128256, meta=None) == E["FLH_E_SCRATCH"]
+    assert _fwd_na(T=262144, H=7168, V=129280, meta=None) == E["FLH_E_SCRATCH"]
