@@ -172,7 +172,7 @@ def clock_snapshot():
     try:
         res = subprocess.run([exe, "--showclocks", "--showmaxpower", "--json"], capture_output=True,
                              text=True, timeout=30)
-        d = json.loads(res.stdout[res.stdout.find("{"):])
+        d, _ = json.JSONDecoder().raw_decode(res.stdout[res.stdout.find("{"):])
     except Exception as e:  # noqa: BLE001 -- reporting only
         out["source"] = f"rocm-smi failed: {type(e).__name__}"
         return out
