@@ -19,6 +19,8 @@ Modules:
   spans coalesced across small gaps, active count.  Pure Python.
 * :mod:`oracle.lmhead` -- fused linear log-prob / entropy forward and backward in
   float64 numpy, by the plain definition (blocked over tokens only).
+* :mod:`oracle.fp8`    -- OCP E4M3 codes decoded to their values, and the fused LM
+  head on FP8 inputs with per-tensor scales (the definition above on the values).
 * :mod:`oracle.tiny`   -- the same forward/backward in pure Python with
   ``math.fsum``, for shapes of a few tokens; a second, loop-level rendering of
   the definition used to cross-check the numpy one.
@@ -28,4 +30,4 @@ docstrings (gap counting, span coordinates, tile bitmap order, entropy in nats,
 no ignore-index for targets).
 """
 
-from . import lmhead, spans, tiny  # noqa: F401
+from . import fp8, lmhead, spans, tiny  # noqa: F401

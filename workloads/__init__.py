@@ -8,4 +8,4 @@ their inputs from.
 
 from .configs import CONFIGS, Config, get_config  # noqa: F401
 from .masks import make_mask  # noqa: F401
-from .inputs import make_tensors, make_upstream  # noqa: F401
+from .inputs import make_tensors, make_tensors_fp8, make_upstream  # noqa: F401

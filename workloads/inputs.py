@@ -55,3 +55,20 @@ def make_upstream(mask: np.ndarray, mode: str = "lp+ent",
     if mode != "lp+ent":
         raise ValueError(mode)
     return a, a.copy()
+
+
+def make_tensors_fp8(T: int, H: int, V: int, seed: int, device="cpu"):
+    """FP8 inputs: (h codes uint8 [T,H], scale_h, W codes uint8 [V,H], scale_w,
+    targets int64 [T]).
+
+    h and W are drawn exactly as by make_tensors (same seed, fp32), then each tensor
+    is given one fp32 scale, amax / 448 (448 = the largest finite OCP E4M3 value), and
+    rounded to E4M3 codes of x / scale by torch's float8_e4m3fn conversion."""
+    h, W, y = make_tensors(T, H, V, "f32", seed, device=device)
+    out = []
+    for x in (h, W):
+        scale = float(x.abs().max().clamp_min(1e-30)) / 448.0
+        scale = float(np.float32(scale))
+        codes = (x / scale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+        out += [codes, scale]
+    return out[0], out[1], out[2], out[3], y
