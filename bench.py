@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2516.6e12     # dense bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8 = 2 * PEAK_BF16  # dense fp8 MFMA (16x16x128 f8f6f4), 5.03 PFLOP/s
 PEAK_FP32_MATRIX = 157.3e12
 HBM_PEAK = 8.0e12
 
@@ -49,6 +50,9 @@ def parse():
                    help="stress workload point (default: its headline 50%%)")
     p.add_argument("--no-hash", action="store_true", help="skip the SHA-256 of the input bytes")
     p.add_argument("--no-secondary", action="store_true", help="skip the tiny fp32 secondary line")
+    p.add_argument("--dtype", choices=["auto", "fp8"], default="auto",
+                   help="fp8: the workload's draws as OCP E4M3 codes with per-tensor scales "
+                        "(flh_forward_fp8 / flh_backward_fp8); auto: the workload's own dtype")
     p.add_argument("--dense", action="store_true", help="dense fallback (no metadata)")
     p.add_argument("--cpu-tokens", type=int, default=1024, help="oracle slice (0 = skip)")
     p.add_argument("--no-trace", action="store_true")
@@ -152,10 +156,12 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def workload_label(cfg, frac):
+def workload_label(cfg, frac, fp8=False):
     """Name of a workload point: the config name, plus the active fraction for the
-    stress workload (whose points differ only in the mask)."""
-    return cfg.name if cfg.cid != 5 else f"{cfg.name} active={frac:.2f}"
+    stress workload (whose points differ only in the mask), plus the input dtype when
+    it is fp8."""
+    name = cfg.name if cfg.cid != 5 else f"{cfg.name} active={frac:.2f}"
+    return name + (" fp8" if fp8 else "")
 
 
 def clock_snapshot():
@@ -201,21 +207,24 @@ def input_sha256(*tensors, chunk=1 << 28):
     return hsh.hexdigest()
 
 
-def aux_bytes(name, T, H, V, esz, A, n_spans, n_splits, ld_wt, ld_t):
-    """Algorithmic bytes per launch of the memory-bound kernels (reads + writes)."""
+def aux_bytes(name, T, H, V, esz, A, n_spans, n_splits, ld_wt, ld_t, in_esz=None):
+    """Algorithmic bytes per launch of the memory-bound kernels (reads + writes).
+    esz: element size of the gradients and transposed copies; in_esz: of h and W
+    (1 for fp8 codes)."""
+    in_esz = in_esz or esz
     n_tiles = -(-T // 128)
     if name == "spans_build":
         return T + 8 * n_spans + 4 * -(-n_tiles // 32) + 8
     if name == "bwd_lists":
         return 4 * -(-n_tiles // 32) + 8 * n_spans + 4 * n_tiles + 8 * (T // 32 + n_spans) + 4 * -(-T // 32)
     if name == "fwd_target_logit":
-        return 2 * T * H * esz + 8 * T + 4 * T
+        return 2 * T * H * in_esz + 8 * T + 4 * T
     if name == "fwd_combine":
         return -(-V // 256) * T * 16 + 4 * T + 12 * T
     if name == "dhidden_finalize":
         return A * H * 4 + T * H * esz + T + 4 * -(-T // 32)
     if name == "transpose":  # the W and h transposes of one backward, per launch on average
-        return ((V * H + n_splits * H * ld_wt) + (T * H + H * ld_t)) * esz / 2
+        return ((V * H + T * H) * in_esz + (n_splits * H * ld_wt + H * ld_t) * esz) / 2
     return None
 
 
@@ -231,14 +240,20 @@ def stored_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(h, W, y, mask, a, b, n_tok):
-    """The fp64 oracle (forward + backward) on the first n_tok tokens, full H and V."""
+def cpu_baseline(h, W, y, mask, a, b, n_tok, scales=None):
+    """The fp64 oracle (forward + backward) on the first n_tok tokens, full H and V.
+    scales: (scale_h, scale_w) when h and W hold fp8 codes (decoded by the oracle)."""
     import threadpoolctl
 
+    from oracle import fp8 as O8
     from oracle import lmhead as O
 
-    hs = h[:n_tok].float().cpu().numpy().astype(np.float64)
-    Wf = W.float().cpu().numpy().astype(np.float64)
+    if scales is not None:
+        hs = O8.dequantize(h[:n_tok].cpu().numpy(), scales[0])
+        Wf = O8.dequantize(W.cpu().numpy(), scales[1])
+    else:
+        hs = h[:n_tok].float().cpu().numpy().astype(np.float64)
+        Wf = W.float().cpu().numpy().astype(np.float64)
     ys = y[:n_tok].cpu().numpy()
     ms = mask[:n_tok]
     info = threadpoolctl.threadpool_info()
@@ -249,7 +264,7 @@ def cpu_baseline(h, W, y, mask, a, b, n_tok):
     dt = time.perf_counter() - t0
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n_tok} tokens of the workload at full H and V, fp64 numpy "
-                      f"forward+backward, {dt:.2f} s"}
+                      f"forward+backward{' on the decoded fp8 inputs' if scales else ''}, {dt:.2f} s"}
 
 
 def tiny_fp32_line(torch, dev, steps=50, warmup=5):
@@ -301,16 +316,20 @@ def main():
         return
     import torch
 
-    from entropy_block_sparse_amd import (flh_backward, flh_forward, flh_spans_build,
-                                          flh_workspace_bytes, trace_begin, trace_end)
-    from workloads import get_config, make_mask, make_tensors, make_upstream
+    from entropy_block_sparse_amd import (flh_backward, flh_backward_fp8, flh_forward, flh_forward_fp8,
+                                          flh_spans_build, flh_workspace_bytes, trace_begin, trace_end)
+    from workloads import get_config, make_mask, make_tensors, make_tensors_fp8, make_upstream
 
     cfg = get_config(args.config)
     dev = torch.device("cuda:0")
     frac_req = args.active_frac if args.active_frac is not None else (cfg.target_active if cfg.cid == 5 else None)
     mask_np, minfo = make_mask(cfg.cid, active_frac=frac_req)
     T, H, V, Ssplit = cfg.T, cfg.H, cfg.V, cfg.vocab_split
-    h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
+    fp8 = args.dtype == "fp8"
+    if fp8:
+        h, s_h, W, s_w, y = make_tensors_fp8(T, H, V, cfg.seed, device=dev)
+    else:
+        h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
     a_np, b_np = make_upstream(mask_np)
     mask = torch.as_tensor(mask_np).to(dev)
     g_lp = torch.as_tensor(a_np).to(dev)
@@ -320,6 +339,11 @@ def main():
 
     def step():
         meta = None if args.dense else flh_spans_build(mask)
+        if fp8:
+            lp, ent, lse = flh_forward_fp8(h, s_h, W, s_w, y, workspace=ws_f, meta=meta,
+                                           skip_inactive=args.skip_fwd and not args.dense)
+            return flh_backward_fp8(h, s_h, W, s_w, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
+                                    skip_inactive_dw=args.skip_dw)
         lp, ent, lse = flh_forward(h, W, y, workspace=ws_f, meta=meta,
                                    skip_inactive=args.skip_fwd and not args.dense)
         dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, mask, meta, Ssplit, workspace=ws_b,
@@ -364,6 +388,10 @@ def main():
     T_fwd = T_at if (args.skip_fwd and not args.dense) else T  # tokens the forward covers
     F_method = pass_flops * (T_fwd + T_at + T_sp + T_dw) if not args.dense else pass_flops * 4 * T
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_FP32_MATRIX
+    # each contraction's own peak: fp8 inputs run the forward and d-logits on fp8 matrix
+    # instructions and the hidden- and weight-gradient products in bf16
+    kpeak = {"fwd_logits_softmax": PEAK_FP8 if fp8 else peak, "dlogits": PEAK_FP8 if fp8 else peak,
+             "dhidden_spans": peak, "dweight": peak}
 
     per_kernel = {}
     for name, split, kms in recs:
@@ -386,7 +414,8 @@ def main():
     w_max = min(V, Ssplit)
     pad = lambda n: (-(-n // 64) * 64) + (64 if (-(-n // 64)) % 2 == 0 else 0)  # noqa: E731
     for k, d in per_kernel.items():
-        nb = aux_bytes(k, T, H, V, esz, A, len(spans), n_sp, pad(w_max), pad(-(-T // 128) * 128))
+        nb = aux_bytes(k, T, H, V, esz, A, len(spans), n_sp, pad(w_max), pad(-(-T // 128) * 128),
+                       1 if fp8 else esz)
         if nb is not None and d["ms_per_launch"] > 0:
             d["alg_bytes_per_launch"] = nb
             d["gbps"] = nb / (d["ms_per_launch"] * 1e-3) / 1e9
@@ -394,19 +423,23 @@ def main():
     if per_kernel:
         dom = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k]["ms"])
         achieved = alg[dom] / (per_kernel[dom]["ms_per_launch"] * 1e-3)
-        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": stored_traffic(dom, workload_label(cfg, frac_req or 0.0))}
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved / 1e12, "peak": kpeak[dom] / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / kpeak[dom],
+                "traffic": stored_traffic(dom, workload_label(cfg, frac_req or 0.0, fp8))}
         for k in per_kernel:
             if k in alg:
                 per_kernel[k]["tflops"] = alg[k] / (per_kernel[k]["ms_per_launch"] * 1e-3) / 1e12
+                per_kernel[k]["frac_of_peak"] = per_kernel[k]["tflops"] * 1e12 / kpeak[k]
 
     sha = None if args.no_hash else input_sha256(h, W, y, mask)
+    # fraction of peak of the whole step with every contraction at its own dtype's peak
+    t_at_peak = (pass_flops * T_fwd / kpeak["fwd_logits_softmax"] + pass_flops * T_at / kpeak["dlogits"]
+                 + pass_flops * T_sp / peak + pass_flops * T_dw / peak) if not args.dense else None
     secondary = None if (args.no_secondary or cfg.cid == 1) else tiny_fp32_line(torch, dev)
 
     cpu = None
     if args.cpu_tokens > 0:
-        cpu = cpu_baseline(h, W, y, mask_np, a_np, b_np, min(args.cpu_tokens, T))
+        cpu = cpu_baseline(h, W, y, mask_np, a_np, b_np, min(args.cpu_tokens, T), (s_h, s_w) if fp8 else None)
 
     out = {
         "metric": "fused LM-head fwd+bwd tokens/sec at 1 GPU + % of bf16 MFMA peak",
@@ -419,13 +452,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "fp8-e4m3 (bf16 gradients)" if fp8 else cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": workload_label(cfg, frac_req or 0.0), "T": T, "H": H, "V": V, "vocab_split": Ssplit,
+        "config": {"workload": workload_label(cfg, frac_req or 0.0, fp8), "T": T, "H": H, "V": V, "vocab_split": Ssplit,
                    "active_frac": minfo["active_frac"], "mask_seed": minfo["seed"],
                    "dense_fallback": bool(args.dense), "skip_inactive_dw": bool(args.skip_dw),
                    "skip_inactive_fwd": bool(args.skip_fwd), "padded_tail": bool(args.padded_tail)},
         "pct_peak_method": F_method / (ms * 1e-3) / peak,
+        "pct_peak_method_per_dtype": (t_at_peak / (ms * 1e-3)) if t_at_peak else None,
         "step_ms": {"mean": ms, "median": float(np.median(step_ms)), "min": float(np.min(step_ms)),
                     "max": float(np.max(step_ms))},
         "active_tokens_per_s": A / (ms * 1e-3),

@@ -12,7 +12,9 @@ from .ops import (  # noqa: F401
     FusedLMHead,
     flh_abi_version,
     flh_backward,
+    flh_backward_fp8,
     flh_forward,
+    flh_forward_fp8,
     flh_span_capacity,
     flh_spans_build,
     flh_tile_m,

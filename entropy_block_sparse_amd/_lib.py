@@ -18,8 +18,9 @@ FLH_OK = 0
 STATUS_NAMES = {
     0: "FLH_OK", 1: "FLH_E_NULL", 2: "FLH_E_SHAPE", 3: "FLH_E_DTYPE", 4: "FLH_E_ALIGN",
     5: "FLH_E_WORKSPACE", 6: "FLH_E_META", 7: "FLH_E_UNSUPPORTED", 8: "FLH_E_HIP", 9: "FLH_E_SCRATCH",
+    10: "FLH_E_SCALE",
 }
-FLH_F32, FLH_BF16 = 0, 1
+FLH_F32, FLH_BF16, FLH_FP8_E4M3 = 0, 1, 2
 OP_SPANS, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 FLH_BWD_SKIP_INACTIVE_DW = 1  # flh_backward_ex options (include/flh.h)
 FLH_BWD_PADDED_TAIL = 2
@@ -68,6 +69,12 @@ SIGNATURES = [
     ("flh_forward_noalloc", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta), _VP,
       ctypes.c_uint32]),
+    ("flh_forward_fp8", ctypes.c_int,
+     [_VP, ctypes.c_float, _VP, ctypes.c_float, _VP, _I64, _I64, _I64, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
+      _VP, _SZ, _VP, ctypes.c_uint32]),
+    ("flh_backward_fp8", ctypes.c_int,
+     [_VP, ctypes.c_float, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
+      _I64, _I64, _I64, _I32, _VP, _VP, _VP, _SZ, _VP, ctypes.c_uint32]),
     ("flh_backward", ctypes.c_int,
      [ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.POINTER(ActiveMeta),
       _I64, _I64, _I64, _I32, _VP, _VP, _VP, _SZ, _VP]),

@@ -39,8 +39,32 @@ const char *const kKernelNames[kIdCount] = {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
-int64_t elt_size(flh_dtype dt) { return dt == FLH_BF16 ? 2 : 4; }
-bool dtype_ok(flh_dtype dt) { return dt == FLH_BF16 || dt == FLH_F32; }
+int64_t elt_size(flh_dtype dt) { return dt == FLH_BF16 ? 2 : (dt == FLH_FP8_E4M3 ? 1 : 4); }
+// element of the d-logits staging and of the transposed copies: bf16 for fp8 inputs
+int64_t stage_esz(flh_dtype dt) { return dt == FLH_F32 ? 4 : 2; }
+bool dtype_ok(flh_dtype dt) { return dt == FLH_BF16 || dt == FLH_F32 || dt == FLH_FP8_E4M3; }
+
+// How a call's contractions run: the launch dtype of the products over H (forward,
+// d-logits), that of the hidden- and weight-gradient products over the bf16 or fp32
+// staging, and the scales of fp8 inputs.
+struct Prec {
+  int kdt;        // 0 fp32, 1 bf16, 2 fp8 E4M3
+  int stage_kdt;  // 0 fp32, 1 bf16
+  float zscale;   // logits = zscale * accumulated products
+  float scale_h;  // dW = scale_h * (D^T widened h codes)
+  float scale_w;  // dH = scale_w * (D widened W codes)
+};
+Prec prec_of(flh_dtype dt, float scale_h = 1.f, float scale_w = 1.f) {
+  if (dt == FLH_FP8_E4M3) return Prec{2, 1, scale_h * scale_w, scale_h, scale_w};
+  return Prec{dt == FLH_BF16 ? 1 : 0, dt == FLH_BF16 ? 1 : 0, 1.f, 1.f, 1.f};
+}
+// fp8 scales: finite and positive, with a product (the logit scale) in [1e-30, 1e30]
+bool scales_ok(float scale_h, float scale_w) {
+  auto fin_pos = [](float x) { return x > 0.f && x <= 3.0e38f; };
+  if (!fin_pos(scale_h) || !fin_pos(scale_w)) return false;
+  const double z = (double)scale_h * (double)scale_w;
+  return z >= 1e-30 && z <= 1e30;
+}
 
 // Sizes shared by both calls: T, V in [1, 2^31); H a positive multiple of one
 // 16-byte chunk.
@@ -90,7 +114,7 @@ BwdLayout bwd_layout(flh_dtype dt, int64_t T, int64_t H, int64_t V, int32_t S) {
   const int64_t ld_max = pad_ld(w_max);
   L.ld_wt = pad_ld(w_max);
   L.ld_t = pad_ld(cdiv(T, kSkipTile) * kSkipTile);  // room for whole 128-token tiles
-  const size_t esz = (size_t)elt_size(dt);
+  const size_t esz = (size_t)stage_esz(dt);
   size_t off = 0;
   L.counts = off;
   off = align_up(off + 64, 256);
@@ -163,6 +187,17 @@ flh_status run(int32_t kid, int32_t split, hipStream_t st, F &&f) {
 
 }  // namespace
 
+namespace {
+flh_status forward_run(const Prec &pr, flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                       int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
+                       const flh_active_meta *meta, void *ws, size_t ws_bytes, void *stream, uint32_t flags);
+flh_status backward_run(const Prec &pr, flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                        const float *lse, const float *entropy, const float *grad_logprob,
+                        const float *grad_entropy, const uint8_t *loss_mask, const flh_active_meta *meta,
+                        int64_t T, int64_t H, int64_t V, int32_t vocab_split, void *d_hidden, void *d_weight,
+                        void *ws, size_t ws_bytes, void *stream, uint32_t flags);
+}  // namespace
+
 // Every check of a forward call except those of the workspace.
 flh_status flh::forward_check(flh_dtype dt, const void *h, const void *W, const int64_t *targets, int64_t T,
                               int64_t H, int64_t V, const float *logprob, const float *entropy,
@@ -196,6 +231,7 @@ const char *flh_status_string(flh_status s) {
     case FLH_E_UNSUPPORTED: return "unsupported request";
     case FLH_E_HIP: return "HIP runtime error";
     case FLH_E_SCRATCH: return "sizes exceed the library's static scratch (flh_forward_noalloc)";
+    case FLH_E_SCALE: return "an fp8 scale is not finite and positive, or their product leaves [1e-30, 1e30]";
   }
   return "unknown status";
 }
@@ -248,6 +284,27 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
                           int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
                           const flh_active_meta *meta, void *ws, size_t ws_bytes, void *stream,
                           uint32_t flags) {
+  if (dt == FLH_FP8_E4M3) return FLH_E_UNSUPPORTED;  // fp8 inputs need their scales: flh_forward_fp8
+  return forward_run(prec_of(dt), dt, h, W, targets, T, H, V, logprob, entropy, lse, meta, ws, ws_bytes, stream,
+                     flags);
+}
+
+flh_status flh_forward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, float scale_w,
+                           const int64_t *targets, int64_t T, int64_t H, int64_t V, float *logprob,
+                           float *entropy, float *lse, const flh_active_meta *meta, void *ws, size_t ws_bytes,
+                           void *stream, uint32_t flags) {
+  if (!scales_ok(scale_h, scale_w)) return FLH_E_SCALE;
+  return forward_run(prec_of(FLH_FP8_E4M3, scale_h, scale_w), FLH_FP8_E4M3, h, W, targets, T, H, V, logprob,
+                     entropy, lse, meta, ws, ws_bytes, stream, flags);
+}
+
+}  // extern "C"
+
+namespace {
+
+flh_status forward_run(const Prec &pr, flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                       int64_t T, int64_t H, int64_t V, float *logprob, float *entropy, float *lse,
+                       const flh_active_meta *meta, void *ws, size_t ws_bytes, void *stream, uint32_t flags) {
   const flh_status chk = flh::forward_check(dt, h, W, targets, T, H, V, logprob, entropy, lse, meta, flags);
   if (chk != FLH_OK) return chk;
   const bool skip = (flags & FLH_FWD_SKIP_INACTIVE) != 0;
@@ -266,6 +323,8 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
   a.W = W;
   a.targets = targets;
   a.part = reinterpret_cast<float *>(ws);
+  a.zscale = pr.zscale;
+  a.out_scale = 1.f;
   flh_status s = FLH_OK;
   if (skip) {
     // the active token tiles, ascending (the list builder without span pieces)
@@ -279,21 +338,25 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
     });
     if (s != FLH_OK) return s;
     const int grid = grid_for(cdiv(V, kTile) * cdiv(a.n_skip_tiles, 2), cus);
-    s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwdSkip, a, grid, st); });
+    s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm(pr.kdt, kFwdSkip, a, grid, st); });
   } else {
     const int grid = grid_for(cdiv(V, kTile) * cdiv(T, kTile), cus);
-    s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm((int)dt, kFwd, a, grid, st); });
+    s = run(kIdFwdGemm, -1, st, [&] { return launch_gemm(pr.kdt, kFwd, a, grid, st); });
   }
   if (s != FLH_OK) return s;
   const uint32_t *skip_bits = skip ? meta->tile_bits : nullptr;
   s = run(kIdFwdTarget, -1, st, [&] {
-    return launch_target_logit((int)dt, T, H, V, h, W, targets, logprob, st, skip_bits);
+    return launch_target_logit(pr.kdt, T, H, V, h, W, targets, logprob, st, skip_bits, pr.zscale);
   });
   if (s != FLH_OK) return s;
   return run(kIdFwdCombine, -1, st, [&] {
     return launch_combine(T, V, a.part, logprob, entropy, lse, st, skip_bits);
   });
 }
+
+}  // namespace
+
+extern "C" {
 
 flh_status flh_backward(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
                         const float *lse, const float *entropy, const float *grad_logprob,
@@ -311,11 +374,37 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
                            const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
                            int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
                            size_t ws_bytes, void *stream, uint32_t flags) {
+  if (dt == FLH_FP8_E4M3) return FLH_E_UNSUPPORTED;  // fp8 inputs need their scales: flh_backward_fp8
+  return backward_run(prec_of(dt), dt, h, W, targets, lse, entropy, grad_logprob, grad_entropy, loss_mask, meta,
+                      T, H, V, vocab_split, d_hidden, d_weight, ws, ws_bytes, stream, flags);
+}
+
+flh_status flh_backward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, float scale_w,
+                            const int64_t *targets, const float *lse, const float *entropy,
+                            const float *grad_logprob, const float *grad_entropy, const uint8_t *loss_mask,
+                            const flh_active_meta *meta, int64_t T, int64_t H, int64_t V, int32_t vocab_split,
+                            void *d_hidden, void *d_weight, void *ws, size_t ws_bytes, void *stream,
+                            uint32_t flags) {
+  if (!scales_ok(scale_h, scale_w)) return FLH_E_SCALE;
+  return backward_run(prec_of(FLH_FP8_E4M3, scale_h, scale_w), FLH_FP8_E4M3, h, W, targets, lse, entropy,
+                      grad_logprob, grad_entropy, loss_mask, meta, T, H, V, vocab_split, d_hidden, d_weight, ws,
+                      ws_bytes, stream, flags);
+}
+
+}  // extern "C"
+
+namespace {
+
+flh_status backward_run(const Prec &pr, flh_dtype dt, const void *h, const void *W, const int64_t *targets,
+                        const float *lse, const float *entropy, const float *grad_logprob,
+                        const float *grad_entropy, const uint8_t *loss_mask, const flh_active_meta *meta,
+                        int64_t T, int64_t H, int64_t V, int32_t vocab_split, void *d_hidden, void *d_weight,
+                        void *ws, size_t ws_bytes, void *stream, uint32_t flags) {
   if (!dtype_ok(dt)) return FLH_E_DTYPE;
   if (flags & ~(uint32_t)(FLH_BWD_SKIP_INACTIVE_DW | FLH_BWD_PADDED_TAIL)) return FLH_E_UNSUPPORTED;
   // the padded probe computes tiles with no live vocabulary row, which the fp32 load
   // path cannot address (it clamps onto the last live row)
-  if ((flags & FLH_BWD_PADDED_TAIL) && dt != FLH_BF16) return FLH_E_UNSUPPORTED;
+  if ((flags & FLH_BWD_PADDED_TAIL) && dt == FLH_F32) return FLH_E_UNSUPPORTED;
   if (!h || !W || !targets || !lse || !entropy || !d_hidden || !d_weight || !ws) return FLH_E_NULL;
   const int32_t S = split_or_default(vocab_split);
   if (!dims_ok(dt, T, H, V) || S <= 0 || S % kTile != 0) return FLH_E_SHAPE;
@@ -362,6 +451,8 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
   a.ld_t = L.ld_t;
   a.dh_acc = reinterpret_cast<float *>(base + L.acc);
   a.dW = d_weight;
+  a.zscale = pr.zscale;
+  a.out_scale = 1.f;
   // without metadata every tile is active and the compact layout is the dense one
   a.compact_dw = (flags & FLH_BWD_SKIP_INACTIVE_DW) && meta ? 1 : 0;
 
@@ -374,6 +465,7 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
                         meta ? reinterpret_cast<uint32_t *>(base + L.covered) : nullptr);
   });
   if (s != FLH_OK) return s;
+  // (fp8 codes are widened to bf16 on the way: the transposed copies feed bf16 products)
   s = run(kIdTranspose, -1, st, [&] {
     return launch_transpose((int)elt_size(dt), W, V, H, base + L.Wt, L.ld_wt, S, st);
   });
@@ -400,28 +492,36 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
     // inactive token tiles: zero staging once per layout (the first split is the widest)
     a.zero_vm = sp == 0 && !a.compact_dw;
     a.zero_tm = sp == 0 || a.ld_d != ld_prev;
-    a.Wt = base + L.Wt + (size_t)sp * (size_t)H * (size_t)L.ld_wt * (size_t)elt_size(dt);
+    a.Wt = base + L.Wt + (size_t)sp * (size_t)H * (size_t)L.ld_wt * (size_t)stage_esz(dt);
     const int32_t tag = (int32_t)sp;
     const int64_t v_tiles = cdiv(a.Ws_grid, kTile);
     s = run(kIdDlogits, tag, st, [&] {
-      return launch_gemm((int)dt, kDlogits, a, grid_for(v_tiles * cdiv(a.n_skip_tiles, 2), cus), st);
+      return launch_gemm(pr.kdt, kDlogits, a, grid_for(v_tiles * cdiv(a.n_skip_tiles, 2), cus), st);
     });
     if (s != FLH_OK) return s;
     s = run(kIdDhidden, tag, st, [&] {
-      return launch_gemm((int)dt, kDhidden, a, grid_for(cdiv(L.span_tile_cap, kPiecesPerTile) * h_tiles, cus),
-                         st);
+      return launch_gemm(pr.stage_kdt, kDhidden, a,
+                         grid_for(cdiv(L.span_tile_cap, kPiecesPerTile) * h_tiles, cus), st);
     });
     if (s != FLH_OK) return s;
     s = run(kIdDweight, tag, st, [&] {
-      return launch_gemm((int)dt, kDweight, a, grid_for(v_tiles * h_tiles, cus), st);
+      GemmArgs aw = a;
+      aw.out_scale = pr.scale_h;
+      return launch_gemm(pr.stage_kdt, pr.kdt == 2 ? kDweightS : kDweight, aw, grid_for(v_tiles * h_tiles, cus),
+                         st);
     });
     if (s != FLH_OK) return s;
   }
   return run(kIdFinalize, -1, st, [&] {
-    return launch_finalize((int)dt, T, H, a.dh_acc, loss_mask,
-                           meta ? reinterpret_cast<const uint32_t *>(base + L.covered) : nullptr, d_hidden, st);
+    return launch_finalize(pr.stage_kdt, T, H, a.dh_acc, loss_mask,
+                           meta ? reinterpret_cast<const uint32_t *>(base + L.covered) : nullptr, d_hidden, st,
+                           pr.scale_w);
   });
 }
+
+}  // namespace
+
+extern "C" {
 
 flh_status flh_trace_begin(int32_t capacity) {
   Trace &tr = trace();

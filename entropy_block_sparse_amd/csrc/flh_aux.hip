@@ -270,6 +270,17 @@ __global__ __launch_bounds__(kBlock) void lists_kernel(int64_t T, const uint32_t
   }
 }
 
+// The value of an OCP E4M3 code as fp32 (exact): sign bit 7, exponent bits 6..3 with
+// bias 7, mantissa bits 2..0; exponent 0 is m/8 * 2^-6; code x1111111 is NaN; no
+// infinities.  For a normal code the fp32 pattern is the code's exponent and mantissa
+// moved up by 20 bits plus (127 - 7) in the exponent field.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  const uint32_t em = c & 0x7fu;
+  const float mag = em >= 8u ? __uint_as_float((em << 20) + (120u << 23)) : (float)em * 0.001953125f;
+  return em == 0x7fu ? __uint_as_float(0x7fc00000u) : __uint_as_float(__float_as_uint(mag) | sign);
+}
+
 // bits: NULL, or the tile bitmap of a forward over active 128-token tiles only; tokens
 // of the other tiles get 0 for all three outputs.
 __device__ __forceinline__ bool tile_skipped(const uint32_t *bits, int64_t t) {
@@ -341,14 +352,15 @@ __global__ __launch_bounds__(64 * kCombWaves) void combine_kernel(int64_t T, int
 
 // The target's logit z_y = h[t] . W[y_t], one wavefront per token: each lane takes
 // 16-byte chunks of both rows, fp32 products and sums, then a butterfly over the wave.
-// Written to out[t] (NaN for a target outside [0, V)).
+// Written to out[t] (NaN for a target outside [0, V)).  E = uint8_t: E4M3 codes, whose
+// values' dot product is multiplied by zscale.
 template <typename E>
 __global__ __launch_bounds__(256) void target_logit_kernel(int64_t T, int64_t H, int64_t V,
                                                            const E *__restrict__ h,
                                                            const E *__restrict__ W,
                                                            const int64_t *__restrict__ targets,
                                                            const uint32_t *__restrict__ bits,
-                                                           float *__restrict__ out) {
+                                                           float *__restrict__ out, float zscale) {
   constexpr int kPer = 16 / sizeof(E);
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -364,7 +376,14 @@ __global__ __launch_bounds__(256) void target_logit_kernel(int64_t T, int64_t H,
   for (int64_t c = (int64_t)lane * kPer; c < H; c += 64 * kPer) {
     const uint4 x = *reinterpret_cast<const uint4 *>(hr + c);
     const uint4 w = *reinterpret_cast<const uint4 *>(wr + c);
-    if constexpr (sizeof(E) == 2) {
+    if constexpr (sizeof(E) == 1) {
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc = __builtin_fmaf(e4m3_to_f32((xs[k] >> (8 * b)) & 0xffu), e4m3_to_f32((ws[k] >> (8 * b)) & 0xffu), acc);
+    } else if constexpr (sizeof(E) == 2) {
       const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -380,7 +399,7 @@ __global__ __launch_bounds__(256) void target_logit_kernel(int64_t T, int64_t H,
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) out[t] = acc;
+  if (lane == 0) out[t] = acc * zscale;
 }
 
 // covered: NULL (every token's row was accumulated), or the bitmap of tokens the
@@ -389,7 +408,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, const float *__restrict__ acc,
                                                        const uint8_t *__restrict__ mask,
                                                        const uint32_t *__restrict__ covered,
-                                                       T *__restrict__ dh) {
+                                                       T *__restrict__ dh, float scale) {
   constexpr int kPer = 16 / sizeof(T);
   const int64_t per_row = H / kPer;
   const int64_t n = T_ * per_row;
@@ -409,8 +428,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, co
     if constexpr (sizeof(T) == 2) {
       uint32_t w[4] = {0u, 0u, 0u, 0u};
       if (act) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(acc + t * H + c);
-        const float4 x1 = *reinterpret_cast<const float4 *>(acc + t * H + c + 4);
+        float4 x0 = *reinterpret_cast<const float4 *>(acc + t * H + c);
+        float4 x1 = *reinterpret_cast<const float4 *>(acc + t * H + c + 4);
+        x0 = make_float4(x0.x * scale, x0.y * scale, x0.z * scale, x0.w * scale);
+        x1 = make_float4(x1.x * scale, x1.y * scale, x1.z * scale, x1.w * scale);
         // pairs rounded to bf16 (nearest, ties to even) by v_cvt_pk_bf16_f32
         auto rne2 = [](float lo, float hi) {
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -425,7 +446,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(int64_t T_, int64_t H, co
       *reinterpret_cast<uint4 *>(dh + t * H + c) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (act) x = *reinterpret_cast<const float4 *>(acc + t * H + c);
+      if (act) {
+        x = *reinterpret_cast<const float4 *>(acc + t * H + c);
+        x = make_float4(x.x * scale, x.y * scale, x.z * scale, x.w * scale);
+      }
       *reinterpret_cast<float4 *>(dh + t * H + c) = x;
     }
   }
@@ -452,16 +476,20 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
 
 hipError_t launch_target_logit(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
                                const int64_t *targets, float *logprob, hipStream_t st,
-                               const uint32_t *skip_bits) {
+                               const uint32_t *skip_bits, float zscale) {
   const unsigned tl_blocks = (unsigned)((T + 3) / 4);
-  if (dtype == 1)
+  if (dtype == 2)
+    hipLaunchKernelGGL(target_logit_kernel<uint8_t>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
+                       reinterpret_cast<const uint8_t *>(h), reinterpret_cast<const uint8_t *>(W), targets,
+                       skip_bits, logprob, zscale);
+  else if (dtype == 1)
     hipLaunchKernelGGL(target_logit_kernel<uint16_t>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
                        reinterpret_cast<const uint16_t *>(h), reinterpret_cast<const uint16_t *>(W),
-                       targets, skip_bits, logprob);
+                       targets, skip_bits, logprob, 1.f);
   else
     hipLaunchKernelGGL(target_logit_kernel<float>, dim3(tl_blocks), dim3(256), 0, st, T, H, V,
                        reinterpret_cast<const float *>(h), reinterpret_cast<const float *>(W), targets,
-                       skip_bits, logprob);
+                       skip_bits, logprob, 1.f);
   return hipGetLastError();
 }
 
@@ -474,7 +502,7 @@ hipError_t launch_combine(int64_t T, int64_t V, const float *part, float *logpro
 }
 
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, const uint8_t *mask,
-                           const uint32_t *covered, void *dh, hipStream_t st) {
+                           const uint32_t *covered, void *dh, hipStream_t st, float scale) {
   const int64_t per = dtype == 1 ? 8 : 4;
   const int64_t n = T * (H / per);
   int64_t blocks = (n + 255) / 256;
@@ -482,10 +510,10 @@ hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc, co
   if (blocks < 1) blocks = 1;
   if (dtype == 1)
     hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, T, H, acc,
-                       mask, covered, reinterpret_cast<uint16_t *>(dh));
+                       mask, covered, reinterpret_cast<uint16_t *>(dh), scale);
   else
     hipLaunchKernelGGL(finalize_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, T, H, acc,
-                       mask, covered, reinterpret_cast<float *>(dh));
+                       mask, covered, reinterpret_cast<float *>(dh), scale);
   return hipGetLastError();
 }
 
@@ -507,16 +535,29 @@ namespace {
 
 constexpr int kTrTile = 64;
 
-template <typename E>
-__global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, int64_t R, int64_t C,
-                                                        E *__restrict__ out, int64_t ld_out, int64_t block,
+// Element conversion on the way through the tile: identity, or an E4M3 code to the
+// bfloat16 pattern of its value (exact: every E4M3 value has at most 4 significant bits
+// and an exponent inside bf16's range).
+template <typename Ein, typename Eout>
+__device__ __forceinline__ Eout tr_convert(Ein x) {
+  if constexpr (sizeof(Ein) == 1)
+    return (Eout)(__float_as_uint(e4m3_to_f32(x)) >> 16);
+  else
+    return x;
+}
+
+template <typename Ein, typename Eout>
+__global__ __launch_bounds__(256) void transpose_kernel(const Ein *__restrict__ in, int64_t R, int64_t C,
+                                                        Eout *__restrict__ out, int64_t ld_out, int64_t block,
                                                         int64_t c_tiles, int64_t r_tiles, int64_t n_tiles,
                                                         const int32_t *__restrict__ row_tiles,
                                                         const int32_t *__restrict__ n_row_tiles) {
   constexpr int kT = kTrTile;
-  constexpr int kV = 16 / sizeof(E);  // elements per 16-byte vector
-  constexpr int kVecRow = kT / kV;    // vectors per tile row
-  __shared__ E tile[kT][kT + kV];     // padded rows
+  constexpr int kVi = 16 / sizeof(Ein);   // input elements per 16-byte vector
+  constexpr int kVo = 16 / sizeof(Eout);  // output elements per 16-byte vector
+  constexpr int kVecRowIn = kT / kVi;     // input vectors per tile row
+  constexpr int kVecRowOut = kT / kVo;    // output vectors per tile column
+  __shared__ Eout tile[kT][kT + kVo];     // padded rows
   const int tid = threadIdx.x;
   const bool gather = row_tiles != nullptr;
   const int64_t R_gather = gather ? (int64_t)n_row_tiles[0] * 128 : 0;
@@ -528,9 +569,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
     const int64_t r0 = blk * block + rb;                                   // row of `in`
     const int64_t R_blk = gather ? R_gather : ((R - blk * block) < block ? (R - blk * block) : block);
     if (gather && rb >= R_blk) continue;  // past the gathered rows: not written (whole workgroup)
-    E *outb = out + blk * C * ld_out;
-    for (int idx = tid; idx < kT * kVecRow; idx += 256) {
-      const int rr = idx / kVecRow, cv = (idx % kVecRow) * kV;
+    Eout *outb = out + blk * C * ld_out;
+    for (int idx = tid; idx < kT * kVecRowIn; idx += 256) {
+      const int rr = idx / kVecRowIn, cv = (idx % kVecRowIn) * kVi;
       const int64_t c = c0 + cv;
       int64_t r = r0 + rr;
       bool live = rb + rr < R_blk;  // a row of this block (rows past it read as 0)
@@ -538,31 +579,31 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
         r = (int64_t)row_tiles[(rb + rr) >> 7] * 128 + ((rb + rr) & 127);
         live = r < R;
       }
-      E v[kV];
-      if (live && c + kV <= C) {
+      Ein v[kVi];
+      if (live && c + kVi <= C) {
         const uint4 x = *reinterpret_cast<const uint4 *>(in + r * C + c);
         __builtin_memcpy(v, &x, 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < kV; ++e) v[e] = (live && c + e < C) ? in[r * C + c + e] : E(0);
+        for (int e = 0; e < kVi; ++e) v[e] = (live && c + e < C) ? in[r * C + c + e] : Ein(0);
       }
 #pragma unroll
-      for (int e = 0; e < kV; ++e) tile[rr][cv + e] = v[e];
+      for (int e = 0; e < kVi; ++e) tile[rr][cv + e] = tr_convert<Ein, Eout>(v[e]);
     }
     __syncthreads();
-    for (int idx = tid; idx < kT * kVecRow; idx += 256) {
-      const int cc = idx / kVecRow, rv = (idx % kVecRow) * kV;
+    for (int idx = tid; idx < kT * kVecRowOut; idx += 256) {
+      const int cc = idx / kVecRowOut, rv = (idx % kVecRowOut) * kVo;
       const int64_t c = c0 + cc, r = rb + rv;  // block-local output column
       if (c >= C || r >= ld_out) continue;
-      E v[kV];
+      Eout v[kVo];
 #pragma unroll
-      for (int e = 0; e < kV; ++e) v[e] = (r + e < R_blk) ? tile[rv + e][cc] : E(0);
-      if (r + kV <= ld_out) {
+      for (int e = 0; e < kVo; ++e) v[e] = (r + e < R_blk) ? tile[rv + e][cc] : Eout(0);
+      if (r + kVo <= ld_out) {
         uint4 x;
         __builtin_memcpy(&x, v, 16);
         *reinterpret_cast<uint4 *>(outb + c * ld_out + r) = x;
       } else {
-        for (int e = 0; e < kV && r + e < ld_out; ++e) outb[c * ld_out + r + e] = v[e];
+        for (int e = 0; e < kVo && r + e < ld_out; ++e) outb[c * ld_out + r + e] = v[e];
       }
     }
     __syncthreads();  // the tile is refilled by the next iteration
@@ -583,12 +624,16 @@ hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void 
   const int64_t n_tiles = n_blocks * r_tiles * c_tiles;
   if (n_tiles <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(n_tiles < (1 << 20) ? n_tiles : (1 << 20));
-  if (esz == 2)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
+  if (esz == 1)
+    hipLaunchKernelGGL((transpose_kernel<uint8_t, uint16_t>), dim3(grid), dim3(256), 0, st,
+                       reinterpret_cast<const uint8_t *>(in), R, C, reinterpret_cast<uint16_t *>(out),
+                       ld_out, block, c_tiles, r_tiles, n_tiles, row_tiles, n_row_tiles);
+  else if (esz == 2)
+    hipLaunchKernelGGL((transpose_kernel<uint16_t, uint16_t>), dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t *>(in), R, C, reinterpret_cast<uint16_t *>(out),
                        ld_out, block, c_tiles, r_tiles, n_tiles, row_tiles, n_row_tiles);
   else
-    hipLaunchKernelGGL(transpose_kernel<float>, dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((transpose_kernel<float, float>), dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const float *>(in), R, C, reinterpret_cast<float *>(out), ld_out,
                        block, c_tiles, r_tiles, n_tiles, row_tiles, n_row_tiles);
   return hipGetLastError();

@@ -73,13 +73,14 @@ constexpr int kLdsBytesDh = 4 * kDhWave > kLdsBytesV2 ? 4 * kDhWave : kLdsBytesV
 // epilogue stages.
 template <typename T, int KIND>
 constexpr int lds_bytes() {
-  return sizeof(T) != 2 ? kLdsBytes
-                        : (KIND == kDlogits || KIND == kDweight ? kLdsBytesDlg
+  return sizeof(T) == 4 ? kLdsBytes
+                        : (KIND == kDlogits || KIND == kDweight || KIND == kDweightS ? kLdsBytesDlg
                                                                 : (KIND == kDhidden ? kLdsBytesDh : kLdsBytesV2));
 }
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <typename T> struct Elt;
+template <> struct Elt<uint8_t> { static constexpr int kPer = 16; };  // OCP E4M3 codes
 template <> struct Elt<uint16_t> { static constexpr int kPer = 8; };  // bf16 bit patterns
 template <> struct Elt<float> { static constexpr int kPer = 4; };
 
@@ -266,10 +267,15 @@ __device__ __forceinline__ void seg(const RowSrc &s, int j, const char *&base, i
 template <typename T, int KIND>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
     const GemmArgs a) {
-  constexpr bool kV2 = sizeof(T) == 2;  // bf16: LDS-direct ring; fp32: register-staged
+  constexpr bool kF8 = sizeof(T) == 1;  // fp8 (OCP E4M3) operands, 16 x 16 x 128 MFMA
+  constexpr bool kV2 = sizeof(T) <= 2;  // bf16 and fp8: LDS-direct ring; fp32: register-staged
   __shared__ __attribute__((aligned(16))) char smem[lds_bytes<T, KIND>()];
-  constexpr int kPer = Elt<T>::kPer;    // elements per 16-byte chunk
+  constexpr int kPer = Elt<T>::kPer;    // operand elements per 16-byte chunk
   constexpr int64_t kEsz = sizeof(T);
+  // d-logits staging element: the input dtype, except bf16 for fp8 inputs
+  using TS = typename std::conditional<kF8, uint16_t, T>::type;
+  constexpr int kSPer = Elt<TS>::kPer;
+  constexpr int64_t kSEsz = sizeof(TS);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -326,9 +332,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t mi = z % m_tiles;
         const int64_t p = n_pairs_gemm + z / m_tiles;
         const int64_t c0 = mi * kTile;
-        const int64_t c1 = imin(c0 + kTile, cdiv(a.Ws_grid, kPer) * kPer);
+        const int64_t c1 = imin(c0 + kTile, cdiv(a.Ws_grid, kSPer) * kSPer);
         // token-major staging: rows of the pair's tokens, columns [c0, c1)
-        constexpr int kChunks = kTile / kPer;
+        constexpr int kChunks = kTile / kSPer;
         char *Dw = const_cast<char *>(Dp);
         for (int idx = tid; a.zero_tm && idx < kTile * kChunks; idx += kThreads) {
           const int row = idx / kChunks;
@@ -336,14 +342,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const int64_t e = 2 * p + (row >> 7);
           if (e >= a.n_skip_tiles) continue;
           const int64_t t = (int64_t)a.tile_list[e] * kSkipTile + (row & 127);
-          const int64_t col = c0 + (int64_t)ch * kPer;
+          const int64_t col = c0 + (int64_t)ch * kSPer;
           if (t < a.T && col < c1)
-            store16_nt(Dw + (t * a.ld_d + col) * kEsz, u32x4{0u, 0u, 0u, 0u});
+            store16_nt(Dw + (t * a.ld_d + col) * kSEsz, u32x4{0u, 0u, 0u, 0u});
         }
         // vocabulary-major staging: rows v in [c0, min(c0 + 256, Ws)), the pair's
         // tokens including the zero padding up to a whole 16-byte chunk
         const int64_t v1 = imin(c0 + kTile, (int64_t)a.Ws);
-        constexpr int kVecTile = kSkipTile / kPer;  // 16-byte vectors per token tile
+        constexpr int kVecTile = kSkipTile / kSPer;  // 16-byte vectors per token tile
         char *Dtw = reinterpret_cast<char *>(a.Dt);
         for (int idx = tid; a.zero_vm && idx < kTile * 2 * kVecTile; idx += kThreads) {
           const int vr = idx / (2 * kVecTile);
@@ -352,9 +358,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           const int64_t e = 2 * p + half;
           const int64_t v = c0 + vr;
           if (e >= a.n_skip_tiles || v >= v1) continue;
-          const int64_t t = (int64_t)a.tile_list[e] * kSkipTile + vec * kPer;
-          if (t < cdiv(a.T, kPer) * kPer)
-            store16_nt(Dtw + (v * a.ld_t + t) * kEsz, u32x4{0u, 0u, 0u, 0u});
+          const int64_t t = (int64_t)a.tile_list[e] * kSkipTile + vec * kSPer;
+          if (t < cdiv(a.T, kSPer) * kSPer)
+            store16_nt(Dtw + (v * a.ld_t + t) * kSEsz, u32x4{0u, 0u, 0u, 0u});
         }
         continue;
       }
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     int64_t mi, ni;
     group_map(L, m_tiles, n_tiles, a.group_m > 0 ? a.group_m : kGroupM, mi, ni);
 
-    if constexpr (KIND == kDweight) {
+    if constexpr (KIND == kDweight || KIND == kDweightS) {
       if (K == 0) {  // weight gradient over no active token tile (compact form): zeros
         const int64_t v_tile = mi * kTile, n_tile = ni * kTile;
         const int n_rows = (int)imin(a.Ws - v_tile, kTile), n_cols = (int)imin(a.H - n_tile, kTile);
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // from global memory into LDS (lane l writes 16 bytes at the instruction's LDS
       // base + 16 l), no VGPRs stage the data; stage kt+1 streams into the other
       // buffer while stage kt is multiplied.
-      constexpr int kBKv = 64;
+      constexpr int kBKv = 128 / (int)sizeof(T);  // K elements per stage: 64 bf16 or 128 fp8
       const int nkv = (int)cdiv(K, kBKv);
       const bool ktail = (K % kBKv) != 0;
       auto swz = [](int r) { return (r >> 1) & 7; };
@@ -662,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         char *lb = smem + (s & 1) * kStage;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if ((int64_t)s * kBKv + load_chunk(k) * 8 >= K) {
+          if ((int64_t)s * kBKv + load_chunk(k) * kPer >= K) {
             *reinterpret_cast<u32x4 *>(lb + (8 * wave + k) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
             *reinterpret_cast<u32x4 *>(lb + kOpStage + (8 * wave + k) * 1024 + lane * 16) =
                 u32x4{0u, 0u, 0u, 0u};
@@ -673,9 +679,119 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       constexpr int kLgkm0 = 0xc07f;  // s_waitcnt lgkmcnt(0) only
       constexpr int kVmNext = kPrefetch ? kVm1 : kVm0;  // a stage's own loads landed
 
+      const int swz_lane = swz(lane & 15);  // same for every fragment row of this lane
+      if constexpr (kF8) {
+        // ============ fp8 (OCP E4M3): one 16 x 16 x 128 MFMA K step per stage ============
+        // A stage holds 128 K elements (128 bytes) per row, the bytes of a bf16 stage, and
+        // one v_mfma_f32_16x16x128_f8f6f4 per (i, j) block consumes all of them: a
+        // fragment is 16 rows x 128 bytes, lane l holding row l % 16 and the 32 bytes at
+        // K byte 32 (l / 16), logical chunks 2 (l / 16) and 2 (l / 16) + 1.  A and B use
+        // the same lane -> K map, so every K element meets itself.  The instruction's
+        // format fields are left at 0: both operands E4M3.
+        //
+        // A stage's 64 MFMAs run in quadrant order: blocks i, j < 4 (MFMA p = 4 i + j), then
+        // i < 4, j >= 4, then i >= 4, j < 4, then i, j >= 4.  So A0..A3 and B0..B3 are
+        // needed from the stage's first MFMA, B4..B7 from MFMA 16 and A4..A7 from MFMA 32,
+        // and the previous stage released A0..A3 after its MFMA 31, B0..B3 after 47 and
+        // the rest at its end.  One set of 16 fragments (128 VGPRs) then suffices: B4..B7
+        // and A4..A7 of a stage are read during its first 32 MFMAs, one fragment beside
+        // every fourth; the barrier before MFMA kBar8 publishes the next stage, whose
+        // A0..A3 and B0..B3 are read right after it, one beside every second MFMA, into
+        // registers this stage no longer needs.  All reads of a stage fall between the
+        // barrier that publishes it and the next one, so after that next barrier its
+        // buffer can take the loads of the stage after next.
+        //
+        // Loads, one beside every third MFMA: the B loads of stage kt + 1 early in stage
+        // kt (before its barrier), the A loads of stage kt + 2 after it.
+        typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+        typedef int i32x8 __attribute__((ext_vector_type(8)));
+        constexpr int kBar8 = 40;
+        static_assert(kBar8 >= 32 && kBar8 + 16 <= 64, "this stage's reads end by MFMA 31, the next stage's fit");
+        auto read_frag8 = [&](int st, int op, int blk) -> u32x8 {
+          const char *lb = smem + (st & 1) * kStage + op * kOpStage;
+          const int R = (op ? wn : wm) * 128 + 16 * blk + (lane & 15);
+          const int c0 = 2 * (lane >> 4);
+          const u32x4 lo = *reinterpret_cast<const u32x4 *>(lb + R * 128 + ((c0 ^ swz_lane) << 4));
+          const u32x4 hi = *reinterpret_cast<const u32x4 *>(lb + R * 128 + (((c0 + 1) ^ swz_lane) << 4));
+          return u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        };
+        u32x8 fa[8], fb[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) fa[f] = fb[f] = u32x8{0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        // A fragment's registers stay allocated to it until the read that replaces it: the
+        // compiler sees the inline MFMA's operands as consumed once it is issued and would
+        // otherwise reuse them for addresses while the 8-pass instruction still reads them.
+        auto keep = [](const u32x8 &x) { asm volatile("" : : "v"(x)); };
+        // `last`: the tile's last stage, with the compiler's MFMA (it then owns the wait
+        // states of the epilogue that reads the accumulators)
+        auto mma8 = [&](bool last, int i, int j) {
+          if (last)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                __builtin_bit_cast(i32x8, fa[i]), __builtin_bit_cast(i32x8, fb[j]), acc[i][j], 0, 0, 0, 0, 0, 0);
+          else
+            asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fa[i]), "v"(fb[j]));
+        };
+        auto kstep8 = [&](int kt, bool last) {
+#pragma unroll
+          for (int p = 0; p < 64; ++p) {
+            if (p < 32 && (p & 3) == 0) {  // this stage's B4..B7, then A4..A7
+              const int f = p >> 2;
+              if (f < 4) {
+                keep(fb[4 + f]);
+                fb[4 + f] = read_frag8(kt, 1, 4 + f);
+              } else {
+                keep(fa[f]);
+                fa[f] = read_frag8(kt, 0, f);
+              }
+            }
+            if (!last && p % 3 == 1 && p / 3 < 8) issue_one(kt + 1, 1, p / 3);  // B loads of kt + 1
+            if (!last && p == 24) issue_pf(kt + 1 + kPfAhead);
+            if (!last && p == kBar8) {
+              __builtin_amdgcn_s_waitcnt(kVmNext);  // this wave's loads of stage kt + 1 have landed
+              fix_tail(kt + 1);
+              __builtin_amdgcn_s_waitcnt(kLgkm0);  // and its reads of stage kt are done
+              __builtin_amdgcn_s_barrier();
+            }
+            if (!last && p >= kBar8 && p < kBar8 + 16 && ((p - kBar8) & 1) == 0) {  // next stage's A0..A3, B0..B3
+              const int f = (p - kBar8) >> 1;
+              if (f < 4) {
+                keep(fa[f]);
+                fa[f] = read_frag8(kt + 1, 0, f);
+              } else {
+                keep(fb[f - 4]);
+                fb[f - 4] = read_frag8(kt + 1, 1, f - 4);
+              }
+            }
+            if (p > kBar8 && (p - kBar8) % 3 == 1 && (p - kBar8) / 3 < 8 && kt + 2 < nkv)
+              issue_one(kt + 2, 0, (p - kBar8) / 3);  // A loads of kt + 2
+            const int q = p >> 4, r = p & 15;
+            mma8(last, ((q & 2) ? 4 : 0) + (r >> 2), ((q & 1) ? 4 : 0) + (r & 3));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+        // ---- prologue: stage 0 loaded and visible, its A0..A3 and B0..B3 read, the A
+        // loads of stage 1 issued ----
+#pragma unroll
+        for (int k8 = 0; k8 < 16; ++k8) issue_one(0, k8 >> 3, k8 & 7);
+        __builtin_amdgcn_s_waitcnt(kVm0);
+        fix_tail(0);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          fa[f] = read_frag8(0, 0, f);
+          fb[f] = read_frag8(0, 1, f);
+        }
+        if (nkv > 1) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) issue_one(1, 0, k);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        for (int kt = 0; kt + 1 < nkv; ++kt) kstep8(kt, false);
+        kstep8(nkv - 1, true);
+      } else {
       // Fragment of block i (16 rows from wbase + 16 i) for K slice q (0, 1: 32 elements,
       // 64 bytes) of a stage: lane l reads row l % 16, logical chunk 4 q + l / 16.
-      const int swz_lane = swz(lane & 15);  // same for every fragment row of this lane
       auto read_frag = [&](const char *op, int wbase, int i, int q) -> u32x4 {
         const int R = wbase + 16 * i + (lane & 15);
         return *reinterpret_cast<const u32x4 *>(op + R * 128 + (((4 * q + (lane >> 4)) ^ swz_lane) << 4));
@@ -788,6 +904,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       }
       kstep0(F0a, F0b, F1a, F1b, nkv - 1, -1, -1, true);
       kstep1(F1a, F1b, F0a, F0b, false, 0);
+      }  // bf16 schedule
       __builtin_amdgcn_s_waitcnt(kVm0);  // prefetches still in flight target LDS
       __syncthreads();  // every wave is done with the ring before epilogues reuse LDS
     }
@@ -862,12 +979,20 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int row_lim = n_rows - row0;  // tile row row0 + off is valid iff off < row_lim
       float4 *xch = reinterpret_cast<float4 *>(smem);
       float st_M[8], st_s[8], st_u[8];
+      // The logits are the accumulators times zscale (1 for bf16 and fp32 inputs; for
+      // fp8 inputs the product of the two tensors' scales, > 0, so the maximum of the
+      // scaled values is the scaled maximum).
+      const float zs = kF8 ? a.zscale : 1.f;
+      const float zl2 = zs * kLog2e;
       auto softmax_states = [&](auto masked) {
         constexpr bool kMasked = decltype(masked)::value;
+        // an invalid row (past the vocabulary) reads as a large negative accumulator: it
+        // never wins the maximum and its exponential is 0 (fp8: the scaled value may reach
+        // -inf, so the exponent is clamped below, where 2^d is 0 and 0 * d adds nothing)
         auto z_at = [&](int i, int j, int x) -> float {
           const float z = acc[i][j][x];
           if constexpr (kMasked)
-            return i * 16 + x < row_lim ? z : -1.0e30f;
+            return i * 16 + x < row_lim ? z : (kF8 ? -3.0e38f : -1.0e30f);
           else
             return z;
         };
@@ -882,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             for (int e = 1; e < 8; ++e) m4[c] = fmaxf(m4[c], z_at(c + 4 * (e >> 2), j, e & 3));
           }
           float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-          mx = max_over_x16_x32(mx);  // the column's 4 lane groups
+          mx = max_over_x16_x32(mx) * zs;  // the column's 4 lane groups; scaled
           const float nm2 = -mx * kLog2e;
           float s4[4], u4[4];
 #pragma unroll
@@ -891,7 +1016,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             u4[c] = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float d = __builtin_fmaf(z_at(c + 4 * (e >> 2), j, e & 3), kLog2e, nm2);
+              float d = __builtin_fmaf(z_at(c + 4 * (e >> 2), j, e & 3), zl2, nm2);
+              if constexpr (kF8 && kMasked) d = fmaxf(d, -1000.f);
               const float ex = __builtin_amdgcn_exp2f(d);
               s4[c] += ex;
               u4[c] = __builtin_fmaf(ex, d, u4[c]);
@@ -941,14 +1067,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     } else if constexpr (KIND == kDlogits) {
       const int64_t v_tile = mi * kTile;  // split-local first column
       const int n_live = (int)imin(a.Ws - v_tile, kTile);
-      const int n_cols = (int)imin(cdiv(a.Ws_grid, kPer) * kPer - v_tile, kTile);  // written columns
-      const int64_t t_pad = cdiv(a.T, kPer) * kPer;  // tokens written, zero padding included
+      const int n_cols = (int)imin(cdiv(a.Ws_grid, kSPer) * kSPer - v_tile, kTile);  // written columns
+      const int64_t t_pad = cdiv(a.T, kSPer) * kSPer;  // tokens written, zero padding included
       // the pair's two token tiles (the second may be missing)
       const int64_t n_act = uni(a.counts[0]);  // active token tiles
       const int64_t pt0 = uni(a.tile_list[2 * ni]);
       const int64_t pt1 = (2 * ni + 1 < a.n_skip_tiles) ? uni(a.tile_list[2 * ni + 1]) : -1;
-      T *Dd = reinterpret_cast<T *>(a.D) + v_tile;
-      T *Dv = reinterpret_cast<T *>(a.Dt) + v_tile * a.ld_t;
+      TS *Dd = reinterpret_cast<TS *>(a.D) + v_tile;
+      TS *Dv = reinterpret_cast<TS *>(a.Dt) + v_tile * a.ld_t;
       // bf16: the tile's d-logits are staged in LDS token-major, Ls[token][vocab] with
       // kLsPitch-byte rows, and both layouts are then written with 16-byte stores.
       char *Ls = smem;
@@ -979,7 +1105,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             float d[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float z = acc[i][j][c];
+              const float z = kF8 ? acc[i][j][c] * a.zscale : acc[i][j][c];  // fp8: codes' product x scales
               const float p = __expf(z - lse_t);
               const float val = ga * ((c0 + c == yl ? 1.f : 0.f) - p) + gb * p * (ez - z);
               d[c] = (c0 + c < lim) ? val : 0.f;
@@ -1118,11 +1244,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int n_cols = (int)imin(a.H - n_tile, kTile);
       T *base = reinterpret_cast<T *>(a.dW) + (a.v_base + v_tile) * a.H + n_tile;
       if constexpr (kV2) {
+        // kDweightS: h^T holds the widened fp8 codes of h, so dW = out_scale * (D^T h^T)
+        const float os = KIND == kDweightS ? a.out_scale : 1.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            ls_put4(col0 + j * 16, row0 + i * 16, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            ls_put4(col0 + j * 16, row0 + i * 16, acc[i][j][0] * os, acc[i][j][1] * os, acc[i][j][2] * os,
+                    acc[i][j][3] * os);
         __syncthreads();
         ls_store_rows(std::false_type{}, reinterpret_cast<char *>(base), a.H, n_rows,
                       [&](int, int cb) -> int64_t { return cb < n_cols ? cb : -1; });
@@ -1161,6 +1290,7 @@ hipError_t launch_t(GemmKind kind, const GemmArgs &a, int grid, hipStream_t st) 
     case kDhidden: return launch_kind<T, kDhidden>(a, grid, st);
     case kDweight: return launch_kind<T, kDweight>(a, grid, st);
     case kFwdSkip: return launch_kind<T, kFwdSkip>(a, grid, st);
+    default: break;
   }
   return hipErrorInvalidValue;
 }
@@ -1169,6 +1299,17 @@ hipError_t launch_t(GemmKind kind, const GemmArgs &a, int grid, hipStream_t st) 
 
 hipError_t launch_gemm(int dtype, GemmKind kind, const GemmArgs &a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
+  if (dtype == 2) {  // fp8 operands: the contractions over H (the hidden- and weight-gradient
+                     // products take bf16 operands and run as dtype 1)
+    switch (kind) {
+      case kFwd: return launch_kind<uint8_t, kFwd>(a, grid, st);
+      case kFwdSkip: return launch_kind<uint8_t, kFwdSkip>(a, grid, st);
+      case kDlogits: return launch_kind<uint8_t, kDlogits>(a, grid, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (kind == kDweightS)
+    return dtype == 1 ? launch_kind<uint16_t, kDweightS>(a, grid, st) : hipErrorInvalidValue;
   return dtype == 1 ? launch_t<uint16_t>(kind, a, grid, st) : launch_t<float>(kind, a, grid, st);
 }
 

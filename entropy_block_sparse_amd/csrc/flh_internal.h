@@ -32,6 +32,7 @@ enum GemmKind : int {
   kDhidden,   // dH[span rows] (+)= D[span rows, :] W_s           (K = W_s; B = W^T rows)
   kDweight,   // dW[split rows] = D^T h                          (K = T; A = D^T rows, B = h^T rows)
   kFwdSkip,   // kFwd over pairs of active 128-token tiles only    (K = H)
+  kDweightS,  // kDweight times out_scale (bf16 operands widened from fp8 codes of h)
 };
 
 // Everything a contraction kernel needs; plain data, passed by value.
@@ -83,9 +84,16 @@ struct GemmArgs {
   int32_t group_m;         // tiles along M in each rasterization group (the 32 tiles
                            // in flight on one XCD form a group_m x 32/group_m block)
   void *dW;                // [V][H]
+  // Logit scale: z = zscale * (accumulated product) in the forward and d-logits
+  // epilogues; 1 for bf16 and fp32 inputs, scale_h * scale_w for fp8 inputs (> 0).
+  float zscale;
+  // Weight-gradient output scale of kDweightS: dW = out_scale * (D^T h^T) with h^T the
+  // widened fp8 codes of h, out_scale = scale_h.
+  float out_scale;
 };
 
-// dtype: 0 = fp32, 1 = bf16 (flh_dtype values)
+// dtype: 0 = fp32, 1 = bf16 (flh_dtype values), 2 = fp8 E4M3 operands (forward,
+// forward over active tiles and d-logits only; their d-logits staging is bf16)
 hipError_t launch_gemm(int dtype, GemmKind kind, const GemmArgs &a, int grid, hipStream_t st);
 
 hipError_t launch_spans(const uint8_t *mask, int64_t T, int32_t max_gap, int32_t tile_m,
@@ -104,9 +112,11 @@ hipError_t launch_lists(int64_t T, const uint32_t *tile_bits, const int32_t *spa
 // Target logits z_y = h[t] . W[y_t] into logprob (NaN for a target outside [0, V)).
 // skip_bits: NULL, or the tile bitmap of a forward over active token tiles only (the
 // other tiles' tokens are left alone).
+// dtype 2: h and W are E4M3 codes, and the dot product of the codes' values is
+// multiplied by zscale.
 hipError_t launch_target_logit(int dtype, int64_t T, int64_t H, int64_t V, const void *h, const void *W,
                                const int64_t *targets, float *logprob, hipStream_t st,
-                               const uint32_t *skip_bits = nullptr);
+                               const uint32_t *skip_bits = nullptr, float zscale = 1.f);
 // The merge of the per-tile softmax states into lse, entropy and logprob = z_y - lse
 // (logprob holds z_y on entry).  skip_bits as above; skipped tokens get 0 for all three.
 hipError_t launch_combine(int64_t T, int64_t V, const float *part, float *logprob, float *entropy,
@@ -120,13 +130,15 @@ hipError_t launch_combine(int64_t T, int64_t V, const float *part, float *logpro
 // Gather form: row_tiles (device, 128-row tiles of `in`) and n_row_tiles (device
 // count) set, block = R: output column r = input row row_tiles[r / 128] * 128 + r % 128,
 // for r < 128 * n_row_tiles[0] only.
+// esz 1: `in` holds E4M3 codes and `out` gets the bf16 values they encode (exact).
 hipError_t launch_transpose(int esz, const void *in, int64_t R, int64_t C, void *out, int64_t ld_out,
                             int64_t block, hipStream_t st, const int32_t *row_tiles = nullptr,
                             const int32_t *n_row_tiles = nullptr);
 
-// dh = acc rounded to the output dtype for active tokens, +0 for inactive ones, NaN
-// for active tokens outside `covered` (NULL: every token covered).
+// dh = scale * acc rounded to the output dtype (0 fp32, 1 bf16) for active tokens, +0
+// for inactive ones, NaN for active tokens outside `covered` (NULL: every token covered).
 hipError_t launch_finalize(int dtype, int64_t T, int64_t H, const float *acc,
-                           const uint8_t *mask, const uint32_t *covered, void *dh, hipStream_t st);
+                           const uint8_t *mask, const uint32_t *covered, void *dh, hipStream_t st,
+                           float scale = 1.f);
 
 }  // namespace flh

@@ -14,8 +14,8 @@ from typing import List, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import (FLH_BF16, FLH_BWD_PADDED_TAIL, FLH_BWD_SKIP_INACTIVE_DW, FLH_F32, FLH_FWD_SKIP_INACTIVE,
-                   OP_BACKWARD, OP_FORWARD, ActiveMeta, check, lib)
+from ._lib import (FLH_BF16, FLH_BWD_PADDED_TAIL, FLH_BWD_SKIP_INACTIVE_DW, FLH_F32, FLH_FP8_E4M3,
+                   FLH_FWD_SKIP_INACTIVE, OP_BACKWARD, OP_FORWARD, ActiveMeta, check, lib)
 
 DEFAULT_MAX_GAP = 128
 DEFAULT_VOCAB_SPLIT = 16384
@@ -73,9 +73,19 @@ def flh_span_capacity(T: int, max_gap: int = DEFAULT_MAX_GAP) -> int:
     return int(lib().flh_span_capacity(int(T), int(max_gap)))
 
 
+def _code_of(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return FLH_BF16
+    if dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FLH_FP8_E4M3
+    return FLH_F32
+
+
 def flh_workspace_bytes(op: int, dtype: torch.dtype, T: int, H: int, V: int,
                         vocab_split: int = 0) -> int:
-    code = FLH_BF16 if dtype == torch.bfloat16 else FLH_F32
+    """dtype: torch.bfloat16, torch.float32, or torch.uint8 / torch.float8_e4m3fn for
+    fp8 (OCP E4M3) inputs."""
+    code = _code_of(dtype)
     return int(lib().flh_workspace_bytes(int(op), code, int(T), int(H), int(V), int(vocab_split)))
 
 
@@ -222,6 +232,86 @@ def flh_backward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
                                  _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V,
                                  int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
                                  _stream(dev)), "flh_backward")
+    return dH, dW
+
+
+# ---- fp8 (OCP E4M3) inputs ---------------------------------------------------------
+
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    return t.contiguous()
+
+
+def _check_operands_fp8(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor):
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError(f"h and W must be 2-D, got {tuple(h.shape)} and {tuple(W.shape)}")
+    T, H = h.shape
+    if W.shape[1] != H:
+        raise ValueError(f"W has {W.shape[1]} columns, h has {H}")
+    if targets.numel() != T:
+        raise ValueError(f"targets has {targets.numel()} elements, h has {T} rows")
+    return int(T), int(H), int(W.shape[0])
+
+
+def flh_forward_fp8(h: torch.Tensor, scale_h: float, W: torch.Tensor, scale_w: float, targets: torch.Tensor,
+                    workspace: Optional[torch.Tensor] = None, meta: Optional["ActiveMetaTensors"] = None,
+                    skip_inactive: bool = False):
+    """Forward on fp8 inputs: h = scale_h * value(h codes), W = scale_w * value(W codes)
+    (OCP E4M3, per-tensor scales).  Returns (logprob, entropy, lse), float32 [T]."""
+    T, H, V = _check_operands_fp8(h, W, targets)
+    h, W = _codes(h, "h"), _codes(W, "W")
+    _require_cuda(h, W, targets)
+    targets = targets.to(torch.int64).contiguous()
+    dev = h.device
+    lp, ent, lse = (torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3))
+    need = flh_workspace_bytes(OP_FORWARD, torch.uint8, T, H, V)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    if skip_inactive and meta is None:
+        raise ValueError("skip_inactive needs the active metadata (flh_spans_build)")
+    mp = ctypes.byref(meta.struct) if (skip_inactive and meta is not None) else None
+    check(lib().flh_forward_fp8(_ptr(h), float(scale_h), _ptr(W), float(scale_w), _ptr(targets), T, H, V,
+                                _ptr(lp), _ptr(ent), _ptr(lse), mp, _ptr(ws), ws.numel(), _stream(dev),
+                                FLH_FWD_SKIP_INACTIVE if skip_inactive else 0), "flh_forward_fp8")
+    return lp, ent, lse
+
+
+def flh_backward_fp8(h: torch.Tensor, scale_h: float, W: torch.Tensor, scale_w: float, targets: torch.Tensor,
+                     lse: torch.Tensor, entropy: torch.Tensor, grad_logprob: Optional[torch.Tensor],
+                     grad_entropy: Optional[torch.Tensor], loss_mask: Optional[torch.Tensor] = None,
+                     meta: Optional[ActiveMetaTensors] = None, vocab_split: int = 0,
+                     workspace: Optional[torch.Tensor] = None, skip_inactive_dw: bool = False):
+    """Backward on fp8 inputs: (d_hidden [T,H], d_weight [V,H]) in bf16, the gradients
+    with respect to the dequantized h and W."""
+    T, H, V = _check_operands_fp8(h, W, targets)
+    for name, t in (("lse", lse), ("entropy", entropy), ("grad_logprob", grad_logprob),
+                    ("grad_entropy", grad_entropy), ("loss_mask", loss_mask)):
+        _check_len(name, t, T)
+    if meta is not None:
+        if loss_mask is None:
+            raise ValueError("active metadata needs the loss mask it was built from")
+        if meta.T != T:
+            raise ValueError(f"active metadata describes {meta.T} tokens, the call has {T}")
+    h, W = _codes(h, "h"), _codes(W, "W")
+    _require_cuda(h, W, targets, lse, entropy, grad_logprob, grad_entropy, loss_mask)
+    targets = targets.to(torch.int64).contiguous()
+    lse, entropy = _f32(lse), _f32(entropy)
+    g_lp, g_ent = _f32(grad_logprob), _f32(grad_entropy)
+    m = _mask_u8(loss_mask)
+    dev = h.device
+    dH = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((V, H), dtype=torch.bfloat16, device=dev)
+    need = flh_workspace_bytes(OP_BACKWARD, torch.uint8, T, H, V, vocab_split)
+    if need == 0:
+        raise ValueError("invalid sizes or vocab_split")
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    mp = ctypes.byref(meta.struct) if meta is not None else None
+    check(lib().flh_backward_fp8(_ptr(h), float(scale_h), _ptr(W), float(scale_w), _ptr(targets), _ptr(lse),
+                                 _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V, int(vocab_split),
+                                 _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev),
+                                 FLH_BWD_SKIP_INACTIVE_DW if skip_inactive_dw else 0), "flh_backward_fp8")
     return dH, dW
 
 

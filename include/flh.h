@@ -83,10 +83,13 @@ typedef enum FLH_ENUM_INT {
   FLH_E_META = 6,        /* active metadata inconsistent with this call              */
   FLH_E_UNSUPPORTED = 7, /* valid request the library does not support               */
   FLH_E_HIP = 8,         /* a HIP runtime call or kernel launch failed               */
-  FLH_E_SCRATCH = 9      /* sizes exceed the static scratch (flh_forward_noalloc)   */
+  FLH_E_SCRATCH = 9,     /* sizes exceed the static scratch (flh_forward_noalloc)   */
+  FLH_E_SCALE = 10       /* an fp8 scale is not usable (flh_forward_fp8/backward_fp8) */
 } flh_status;
 
-typedef enum FLH_ENUM_INT { FLH_F32 = 0, FLH_BF16 = 1 } flh_dtype;
+/* FLH_FP8_E4M3: OCP E4M3 codes (see flh_forward_fp8); accepted by the queries
+ * (flh_tile_m, flh_workspace_bytes) and the fp8 entry points only. */
+typedef enum FLH_ENUM_INT { FLH_F32 = 0, FLH_BF16 = 1, FLH_FP8_E4M3 = 2 } flh_dtype;
 
 /* Which call a workspace size is for. */
 typedef enum FLH_ENUM_INT { FLH_OP_SPANS = 0, FLH_OP_FORWARD = 1, FLH_OP_BACKWARD = 2 } flh_op;
@@ -192,6 +195,29 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
                           void *stream, uint32_t flags);
 
 /*
+ * FP8 inputs.  The pages list FP8 among the layouts the span builder serves (SkyRL
+ * #2376, Bugbot "Overview") and give no recipe; these calls take h and W as codes of
+ * the OCP E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; x1111111 is NaN; largest finite 448) with one fp32 scale per tensor:
+ *   h[t,k] = scale_h * value(h[t,k]),   W[v,k] = scale_w * value(W[v,k]),
+ * and compute on those values exactly what flh_forward_ex / flh_backward_ex compute
+ * (definitions above).  The contractions over H (forward, d-logits) run on the codes
+ * with fp8 matrix instructions and fp32 accumulation, the logits being the accumulated
+ * products times scale_h * scale_w; the hidden- and weight-gradient products run in
+ * bf16 on the codes widened exactly to bf16, with scale_w and scale_h applied to their
+ * fp32 results.
+ *   h [T,H], W [V,H]: uint8 codes, row-major, 16-byte aligned; H a multiple of 16.
+ *   scale_h, scale_w: finite and > 0, with scale_h * scale_w in [1e-30, 1e30], else
+ *   FLH_E_SCALE.
+ *   Workspace: flh_workspace_bytes(op, FLH_FP8_E4M3, ...).
+ * flh_forward_fp8: arguments, options (FLH_FWD_*) and outputs as flh_forward_ex.
+ */
+flh_status flh_forward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, float scale_w,
+                           const int64_t *targets, int64_t T, int64_t H, int64_t V, float *logprob,
+                           float *entropy, float *lse, const flh_active_meta *meta, void *ws,
+                           size_t ws_bytes, void *stream, uint32_t flags);
+
+/*
  * flh_forward_ex for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same call
  * without a workspace argument.  Its scratch (the per-tile softmax states and the
@@ -269,7 +295,7 @@ enum {
 /*
  * flh_backward with options: `flags` is a bitwise OR of FLH_BWD_* values (0 gives
  * flh_backward).  Arguments, workspace and errors as for flh_backward, and
- * FLH_E_UNSUPPORTED for an unknown flag bit.
+ * FLH_E_UNSUPPORTED for an unknown flag bit.  (dt FLH_FP8_E4M3: flh_backward_fp8.)
  */
 flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
                            const float *lse, const float *entropy, const float *grad_logprob,
@@ -277,6 +303,20 @@ flh_status flh_backward_ex(flh_dtype dt, const void *h, const void *W, const int
                            const flh_active_meta *meta, int64_t T, int64_t H, int64_t V,
                            int32_t vocab_split, void *d_hidden, void *d_weight, void *ws,
                            size_t ws_bytes, void *stream, uint32_t flags);
+
+/*
+ * Backward for FP8 inputs (see flh_forward_fp8): d_hidden [T,H] and d_weight [V,H] in
+ * bf16 (gradients with respect to the dequantized h and W), from the lse and entropy
+ * flh_forward_fp8 saved.  Other arguments, options (FLH_BWD_*) and errors as for
+ * flh_backward_ex, plus FLH_E_SCALE.
+ */
+flh_status flh_backward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, float scale_w,
+                            const int64_t *targets, const float *lse, const float *entropy,
+                            const float *grad_logprob, const float *grad_entropy,
+                            const uint8_t *loss_mask, const flh_active_meta *meta, int64_t T,
+                            int64_t H, int64_t V, int32_t vocab_split, void *d_hidden,
+                            void *d_weight, void *ws, size_t ws_bytes, void *stream,
+                            uint32_t flags);
 
 /*
  * Launch tracing (profiling aid).  Between flh_trace_begin and flh_trace_end on

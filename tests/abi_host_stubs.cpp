@@ -15,7 +15,7 @@ hipError_t launch_lists(int64_t, const uint32_t *, const int32_t *, const int32_
   return hipErrorInvalidValue;
 }
 hipError_t launch_target_logit(int, int64_t, int64_t, int64_t, const void *, const void *, const int64_t *,
-                               float *, hipStream_t, const uint32_t *) {
+                               float *, hipStream_t, const uint32_t *, float) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_combine(int64_t, int64_t, const float *, float *, float *, float *, hipStream_t,
@@ -27,7 +27,7 @@ hipError_t launch_transpose(int, const void *, int64_t, int64_t, void *, int64_t
   return hipErrorInvalidValue;
 }
 hipError_t launch_finalize(int, int64_t, int64_t, const float *, const uint8_t *, const uint32_t *, void *,
-                           hipStream_t) {
+                           hipStream_t, float) {
   return hipErrorInvalidValue;
 }
 }  // namespace flh

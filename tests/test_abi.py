@@ -22,7 +22,7 @@ def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
-    return sorted(set(re.findall(r"\b(flh_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(flh_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -41,7 +41,7 @@ def test_abi_version_and_queries():
     assert L.flh_span_capacity(16384, 128) == 127
     assert L.flh_span_capacity(262144, 128) == 2017
     assert L.flh_span_capacity(0, 128) == 0 and L.flh_span_capacity(10, -1) == 0
-    for s in range(10):
+    for s in range(11):
         assert L.flh_status_string(s)
 
 
@@ -213,3 +213,37 @@ def test_noalloc_forward_validation():
     assert L.flh_workspace_bytes(1, 1, 16744, 4096, 128256, 0) > cap
     assert _fwd_na(T=16744, H=4096, V=128256, meta=None) == E["FLH_E_SCRATCH"]
     assert _fwd_na(T=262144, H=7168, V=129280, meta=None) == E["FLH_E_SCRATCH"]
+
+
+def _fwd8(sh=0.01, sw=0.001, H=256, T=512, V=4096, h=FAKE, flags=0, meta=None, nbytes=1 << 40):
+    mp = ctypes.byref(meta) if meta is not None else None
+    return lib().flh_forward_fp8(h, sh, FAKE, sw, FAKE, T, H, V, FAKE, FAKE, FAKE, mp, FAKE, nbytes, None, flags)
+
+
+def _bwd8(sh=0.01, sw=0.001, H=256, flags=0):
+    m = _meta(T=512)
+    return lib().flh_backward_fp8(FAKE, sh, FAKE, sw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(m),
+                                  512, H, 4096, 0, FAKE, FAKE, FAKE, 1 << 40, None, flags)
+
+
+def test_fp8_entry_point_validation():
+    """fp8 inputs: scales must be finite and positive with a usable product, rows of
+    codes whole 16-byte chunks; the generic entry points refuse the fp8 dtype (it needs
+    its scales)."""
+    L = lib()
+    inf = float("inf")
+    for sh, sw in ((0.0, 1.0), (-1.0, 1.0), (1.0, inf), (float("nan"), 1.0), (1e-20, 1e-20), (1e20, 1e20)):
+        assert _fwd8(sh, sw) == E["FLH_E_SCALE"], (sh, sw)
+        assert _bwd8(sh, sw) == E["FLH_E_SCALE"], (sh, sw)
+    assert _fwd8(H=24) == E["FLH_E_SHAPE"] and _bwd8(H=24) == E["FLH_E_SHAPE"]   # H % 16
+    assert _fwd8(h=None) == E["FLH_E_NULL"]
+    assert _fwd8(h=FAKE_ODD) == E["FLH_E_ALIGN"]
+    assert _fwd8(flags=1) == E["FLH_E_META"]
+    assert _fwd8(nbytes=100) == E["FLH_E_WORKSPACE"]
+    assert _bwd8(flags=1 << 6) == E["FLH_E_UNSUPPORTED"]
+    assert _fwd(dt=2) == E["FLH_E_UNSUPPORTED"] and _bwd(dt=2) == E["FLH_E_UNSUPPORTED"]
+    # workspace: the forward's does not depend on the input dtype; the backward's staging
+    # and transposed copies are bf16 for fp8 inputs
+    assert L.flh_workspace_bytes(1, 2, 512, 256, 4096, 0) == L.flh_workspace_bytes(1, 1, 512, 256, 4096, 0)
+    assert L.flh_workspace_bytes(2, 2, 512, 256, 4096, 0) == L.flh_workspace_bytes(2, 1, 512, 256, 4096, 0)
+    assert L.flh_workspace_bytes(1, 2, 512, 24, 4096, 0) == 0 and L.flh_tile_m(2) == 128

@@ -133,15 +133,18 @@ def span_pieces(spans, piece=PIECE):
     return out
 
 
-def transpose_model(inp, R, C, out, ld_out, esz, what, block=0, tiles=None):
+def transpose_model(inp, R, C, out, ld_out, esz, what, block=0, tiles=None, esz_in=None):
     """Blocked transpose over 64 x 64 tiles: block b of `block` rows of `in` becomes
     out_b = out + b * C * ld_out, [C][ld_out].  16-byte loads where the vector is whole,
     element loads otherwise; stores likewise.  Gather form (`tiles`: the 128-row tiles
     to take, one block): output column r is input row tiles[r // 128] * 128 + r % 128,
     columns from 128 * len(tiles) on are not written.  Checks bounds and that every
     output element (block, c < C, r < ld_out, or r < 128 * len(tiles)) is written
-    exactly once."""
+    exactly once.  esz_in: element size of `in` when it differs (fp8 codes widened to
+    bf16): 16-byte loads of 16 // esz_in elements."""
+    esz_in = esz_in or esz
     kV = 16 // esz
+    kVi = 16 // esz_in
     block = block or R
     n_blocks = cdiv(R, block)
     written = np.zeros((n_blocks, C, ld_out), np.int32)
@@ -153,19 +156,20 @@ def transpose_model(inp, R, C, out, ld_out, esz, what, block=0, tiles=None):
                 continue
             for c0t in range(cdiv(C, 64)):
                 rb, c0 = t0 * 64, c0t * 64
-                idx = np.arange(64 * (64 // kV))
-                rr, cv = idx // (64 // kV), (idx % (64 // kV)) * kV
+                idx = np.arange(64 * (64 // kVi))
+                rr, cv = idx // (64 // kVi), (idx % (64 // kVi)) * kVi
                 r, c = blk * block + rb + rr, c0 + cv
                 live = rb + rr < R_blk
                 if tiles is not None:
                     src = np.where(live, np.array([tiles[min(x, len(tiles) - 1)] for x in (rb + rr) >> 7]), 0)
                     r = src * 128 + ((rb + rr) & 127)
                     live = live & (r < R)
-                whole = live & (c + kV <= C)
-                inp.check((r[whole] * C + c[whole]) * esz, 16, what + " load")
-                for e in range(kV):
+                whole = live & (c + kVi <= C)
+                inp.check((r[whole] * C + c[whole]) * esz_in, 16, what + " load")
+                for e in range(kVi):
                     ok = ~whole & live & (c + e < C)
-                    inp.check((r[ok] * C + c[ok] + e) * esz, esz, what + " load1")
+                    inp.check((r[ok] * C + c[ok] + e) * esz_in, esz_in, what + " load1")
+                idx = np.arange(64 * (64 // kV))
                 cc, rv = idx // (64 // kV), (idx % (64 // kV)) * kV
                 c, r = c0 + cc, rb + rv
                 live = (c < C) & (r < ld_out)
@@ -227,13 +231,16 @@ def dlg_epilogue_v2(D, Dt, pair, T, ld_d, ld_t, t_pad, v0, n_live, n_cols, ni=0,
         Dt.check(((v0 + mb[ok] + li[ok]) * ld_t + t[ok]) * 2, 16, "dlg store^T (LDS)")
 
 
-def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False):
+def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False, in_esz=None):
     """Walks every (sampled) workgroup tile of the four contractions and checks loads
-    (per the fp32 or bf16 load path) and epilogue stores against the buffers."""
+    (per the fp32 or bf16 load path) and epilogue stores against the buffers.
+    in_esz: element size of h and W when it differs from the staging's (fp8 inputs: 1,
+    with bf16 staging and transposed copies, esz = 2)."""
+    in_esz = in_esz or esz
     kper = 16 // esz
     v2 = esz == 2
-    h = Buf("h", T * H * esz)
-    W = Buf("W", V * H * esz)
+    h = Buf("h", T * H * in_esz)
+    W = Buf("W", V * H * in_esz)
     w_max = min(V, S_split)
     ld_max = pad_ld(w_max)
     ld_wt, ld_t = pad_ld(w_max), pad_ld(cdiv(T, SKIP) * SKIP)
@@ -257,7 +264,7 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False
     col_q = (wave & 1) * 128 + (lane & 15)        # + j*16
 
     # ---- forward ----
-    ldb = H * esz
+    ldb = H * in_esz
     for mi, ni in itertools.product(_pick(cdiv(V, TILE), sample), _pick(cdiv(T, TILE), sample)):
         v0, t0 = mi * TILE, ni * TILE
         loads(Src.rows(W, v0 * ldb, V - v0, ldb), H, "fwd A")
@@ -267,7 +274,7 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False
 
     # ---- backward: transposed copies, work lists ----
     if not sample:
-        transpose_model(W, V, H, Wt, ld_wt, esz, "W^T", block=S_split)
+        transpose_model(W, V, H, Wt, ld_wt, esz, "W^T", block=S_split, esz_in=in_esz)
     flags = S.tile_flags(mask, SKIP)
     n_skip = len(flags)
     tile_list = [i for i, f in enumerate(flags) if f] + [i for i, f in enumerate(flags) if not f]
@@ -287,7 +294,8 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False
                 t = tl * SKIP + np.arange(128)
                 part.check((mi * T + t[t < T]) * 16, 16, "fwd-skip part")
     if not sample:
-        transpose_model(h, T, H, ht, ld_t, esz, "h^T", tiles=tile_list[:n_act] if compact else None)
+        transpose_model(h, T, H, ht, ld_t, esz, "h^T", tiles=tile_list[:n_act] if compact else None,
+                        esz_in=in_esz)
     pieces = span_pieces(S.active_spans(mask, 128))
     dh_tiles = [pieces[PIECES_PER_TILE * m:PIECES_PER_TILE * (m + 1)]
                 for m in range(cdiv(len(pieces), PIECES_PER_TILE))]
@@ -434,6 +442,25 @@ def model(T, H, V, S_split, esz, mask, sample=False, compact=False, padded=False
             for quarter in range(4):
                 banks = {((addrs[x] // 4) + b) % 64 for x in range(16 * quarter, 16 * quarter + 16) for b in range(4)}
                 assert len(banks) == 64
+        if in_esz == 1:
+            # fp8 fragments: lane l reads row l % 16, logical chunks 2 (l / 16) and + 1 (the 32
+            # bytes at K byte 32 (l / 16)); each of the two reads covers the 64 banks per
+            # quarter-wave, and the 8 chunks of a row are read once per fragment
+            for i, wb in itertools.product(range(8), (0, 128)):
+                seen = set()
+                for hh in range(2):
+                    addrs = []
+                    for l in range(64):
+                        R = wb + 16 * i + (l & 15)
+                        a = R * 128 + ((((2 * (l >> 4) + hh) ^ ((R >> 1) & 7))) << 4)
+                        assert a + 16 <= OPSTAGE
+                        addrs.append(a)
+                        seen.add(a)
+                    for quarter in range(4):
+                        banks = {((addrs[x] // 4) + b) % 64 for x in range(16 * quarter, 16 * quarter + 16)
+                                 for b in range(4)}
+                        assert len(banks) == 64
+                assert len(seen) == 16 * 8  # 16 rows x 8 chunks, each once
 
 
 SHAPES = [
@@ -453,6 +480,20 @@ def test_fp32_addressing_in_bounds(T, H, V, S_split):
         model(T, H, V, S_split, esz, mask, compact=True)
 
 
+FP8_SHAPES = [(1, 16, 1, 256), (130, 16, 257, 256), (1000, 528, 5000, 2048), (777, 128, 2600, 1024),
+              (257, 80, 263, 256)]
+
+
+@pytest.mark.parametrize("T,H,V,S_split", FP8_SHAPES)
+def test_fp8_addressing_in_bounds(T, H, V, S_split):
+    """fp8 inputs (1-byte codes, H a multiple of 16): the forward and d-logits read the
+    codes through the LDS-direct path; staging and transposed copies are bf16."""
+    rng = np.random.default_rng(T + V)
+    for mask in (np.ones(T, np.uint8), (rng.random(T) < 0.4).astype(np.uint8)):
+        model(T, H, V, S_split, 2, mask, in_esz=1)
+        model(T, H, V, S_split, 2, mask, compact=True, in_esz=1)
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_kernel_addressing_full_workloads_sampled(cid):
     """Boundary tiles and K stages at the full workload shapes (32-bit offsets)."""
@@ -464,6 +505,7 @@ def test_kernel_addressing_full_workloads_sampled(cid):
           compact=True)
     if cfg.dtype == "bf16":
         model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2, mask, sample=True, padded=True)
+        model(cfg.T, cfg.H, cfg.V, cfg.vocab_split, 2, mask, sample=True, in_esz=1)
 
 
 # ---- bf16 path: LDS-direct buffer loads ------------------------------------------------

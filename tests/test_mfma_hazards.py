@@ -17,6 +17,10 @@ windows:
 * after an MFMA, no VALU instruction overwrites its A/B operands within 6 wait
   states.
 
+The fp8 main loop's v_mfma_f32_16x16x128_f8f6f4 takes 8 passes with fp8 operands;
+for it the windows are those of a 16-pass operation (19 wait states after, 11 for
+its A/B operands), above what 8 passes require.
+
 Only MFMAs issued from inline assembly are checked (the listing brackets them with
 ASMSTART / ASMEND markers), but against every instruction around them, the
 compiler's included: for its builtin MFMAs the compiler inserts the wait states
@@ -40,6 +44,12 @@ from entropy_block_sparse_amd import build as B
 W_AFTER = 11
 W_BEFORE_VALU = 3
 W_AB_WAR = 6
+# windows per MFMA mnemonic where they differ from the 4-pass defaults
+LONG_MFMA = {"v_mfma_f32_16x16x128_f8f6f4": (19, 11)}
+
+
+def windows(op):
+    return LONG_MFMA.get(op, (W_AFTER, W_AB_WAR))
 
 REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
 
@@ -197,18 +207,19 @@ def check(asm, kernel_filter=None):
             for idx, m in enumerate(blocks[lb]):
                 if not (m.is_mfma and m.from_asm):
                     continue
-                for ins, ws in walk_forward(blocks, succ, lb, idx, W_AFTER):
+                w_after, w_war = windows(m.op)
+                for ins, ws in walk_forward(blocks, succ, lb, idx, w_after):
                     if ins.is_mfma and ins.dst == m.dst and ins.src_c == m.dst and not (ins.src_ab & m.dst):
                         continue
                     if (ins.reads | ins.writes) & m.dst:
                         problems.append((name, lb, m.text, ins.text, ws, "result used too early"))
-                for ins, ws in walk_forward(blocks, succ, lb, idx, W_AB_WAR):
+                for ins, ws in walk_forward(blocks, succ, lb, idx, w_war):
                     if ins.is_valu and ins.writes & m.src_ab:
                         problems.append((name, lb, m.text, ins.text, ws, "A/B operand overwritten too early"))
-                for ins, ws in walk_backward(blocks, pred, lb, idx, W_AFTER):
+                for ins, ws in walk_backward(blocks, pred, lb, idx, max(W_AFTER, *(w[0] for w in LONG_MFMA.values()))):
                     if ins.is_valu and ws < W_BEFORE_VALU and ins.writes & (m.src_ab | m.src_c):
                         problems.append((name, lb, m.text, ins.text, ws, "operand written by VALU too late"))
-                    if ins.is_mfma and ins.writes & m.src_ab:
+                    if ins.is_mfma and ins.writes & m.src_ab and ws < windows(ins.op)[0]:
                         problems.append((name, lb, m.text, ins.text, ws, "A/B operand written by MFMA too late"))
     return problems
 
@@ -234,6 +245,9 @@ def test_contraction_kernels_respect_matrix_core_wait_states(kernel_asm):
     n_asm = sum(i.is_mfma and i.from_asm for blocks, *_ in parse_kernels(kernel_asm).values()
                 for b in blocks.values() for i in b)
     assert n_asm > 0, "expected the bf16 main loop to issue its MFMAs from inline assembly"
+    n_f8 = sum(i.is_mfma and i.from_asm and i.op == "v_mfma_f32_16x16x128_f8f6f4"
+               for blocks, *_ in parse_kernels(kernel_asm).values() for b in blocks.values() for i in b)
+    assert n_f8 > 0, "expected the fp8 main loop to issue its MFMAs from inline assembly"
     assert not problems, "\n".join(f"{n[-40:]} {lb}: {m}  ->  {i}  (after {ws} wait states: {why})"
                                    for n, lb, m, i, ws, why in problems[:20])
 
