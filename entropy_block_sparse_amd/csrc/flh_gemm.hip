@@ -616,9 +616,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       };
       setup(std::integral_constant<bool, kSplitA>{}, srcA, ra0, ra1, a_vo);
       setup(std::false_type{}, srcB, rb, rb, b_vo);
+      // LDS offset of operand op (0 = A, 1 = B) of stage s: bf16 [A0 B0 | A1 B1]; fp8
+      // [A0 A1 | B0 B1], so that each operand's two stages lie within one 16-bit ds_read
+      // offset of a per-lane base (the fp8 loop then reads with no address arithmetic)
+      auto stage_op = [](int s, int op) -> int {
+        return kF8 ? op * 2 * kOpStage + (s & 1) * kOpStage : (s & 1) * kStage + op * kOpStage;
+      };
       // load k (0..7) of operand op (0 = A, 1 = B) of stage s
       auto issue_one = [&](int s, int op, int k) {
-        char *lb = smem + (s & 1) * kStage + op * kOpStage + (8 * wave + k) * 1024;
+        char *lb = smem + stage_op(s, op) + (8 * wave + k) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : (kSplitA && k >= 4 ? ra1 : ra0), lb, 16,
                                                  op ? b_vo[k] : a_vo[k], s * 128, 0, 0);
       };
@@ -665,12 +671,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       // vocabulary-major staging.
       auto fix_tail = [&](int s) {
         if (!(ktail && s == nkv - 1)) return;
-        char *lb = smem + (s & 1) * kStage;
+        char *lb = smem + stage_op(s, 0);
+        constexpr int kBOff = kF8 ? 2 * kOpStage : kOpStage;  // B relative to A of the same stage
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if ((int64_t)s * kBKv + load_chunk(k) * kPer >= K) {
             *reinterpret_cast<u32x4 *>(lb + (8 * wave + k) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(lb + kOpStage + (8 * wave + k) * 1024 + lane * 16) =
+            *reinterpret_cast<u32x4 *>(lb + kBOff + (8 * wave + k) * 1024 + lane * 16) =
                 u32x4{0u, 0u, 0u, 0u};
           }
       };
@@ -705,14 +712,50 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         // kt (before its barrier), the A loads of stage kt + 2 after it.
         typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
         typedef int i32x8 __attribute__((ext_vector_type(8)));
-        constexpr int kBar8 = 40;
-        static_assert(kBar8 >= 32 && kBar8 + 16 <= 64, "this stage's reads end by MFMA 31, the next stage's fit");
-        auto read_frag8 = [&](int st, int op, int blk) -> u32x8 {
-          const char *lb = smem + (st & 1) * kStage + op * kOpStage;
-          const int R = (op ? wn : wm) * 128 + 16 * blk + (lane & 15);
+        // Schedule (MFMA indices p of a stage): this stage's B4..B7, A4..A7 read beside
+        // p = kCurRd8 * f (f = 0..7); B loads of the next stage beside p = kB0_8 + kLoad8 m;
+        // the L2 prefetch at kPf8At; the barrier before p = kBar8; the next stage's A0..A3
+        // read beside kBar8 + 2 f, its B0..B3 beside kNxB8 + 2 f (B_j is last used at
+        // p = 44 + j); A loads of the stage after next beside kBar8 + 1 + kLoad8 m.
+        constexpr int kBar8 = 40, kLoad8 = 3, kB0_8 = 1, kCurRd8 = 4, kPf8At = 24;
+        constexpr int kNxB8 = kBar8 + 8 > 48 ? kBar8 + 8 : 48;
+        static_assert(4 * kCurRd8 <= 16 && 7 * kCurRd8 < kBar8, "B4.. read by MFMA 16, A7 before the barrier");
+        static_assert(kB0_8 + 7 * kLoad8 < kPf8At && kPf8At < kBar8, "B loads, then the prefetch, before the barrier");
+        static_assert(kBar8 + 1 + 7 * kLoad8 <= 63 && kNxB8 + 6 <= 63, "the stage's tail holds its loads and reads");
+        // This lane's byte offsets of its two chunks in row (lane % 16) of block 0 of each
+        // operand's buffer-0 stage; block blk of a stage in buffer b is at these plus
+        // b * kOpStage + 2048 blk.  Each stage adds its buffer's term once, at its start
+        // (`FragBase`, pinned in registers), so that a fragment read takes no address
+        // arithmetic: every fragment register stays live until the read that replaces it
+        // (see keep below), and an address computed between the two could otherwise land
+        // in registers an 8-pass MFMA is still reading.
+        int ro[2][2];
+        {
           const int c0 = 2 * (lane >> 4);
-          const u32x4 lo = *reinterpret_cast<const u32x4 *>(lb + R * 128 + ((c0 ^ swz_lane) << 4));
-          const u32x4 hi = *reinterpret_cast<const u32x4 *>(lb + R * 128 + (((c0 + 1) ^ swz_lane) << 4));
+#pragma unroll
+          for (int op = 0; op < 2; ++op)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              ro[op][hh] = stage_op(0, op) + ((op ? wn : wm) * 128 + (lane & 15)) * 128 + (((c0 + hh) ^ swz_lane) << 4);
+        }
+        struct FragBase {
+          int o[2][2];
+        };
+        auto frag_base = [&](int st) -> FragBase {
+          FragBase b;
+#pragma unroll
+          for (int op = 0; op < 2; ++op)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              b.o[op][hh] = ro[op][hh] + (st & 1) * kOpStage;
+              asm volatile("" : "+v"(b.o[op][hh]));  // computed here, not next to a read
+            }
+          return b;
+        };
+        auto read_frag8 = [&](const FragBase &b, int op, int blk) -> u32x8 {
+          const char *lb = smem + 2048 * blk;
+          const u32x4 lo = *reinterpret_cast<const u32x4 *>(lb + b.o[op][0]);
+          const u32x4 hi = *reinterpret_cast<const u32x4 *>(lb + b.o[op][1]);
           return u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         };
         u32x8 fa[8], fb[8];
@@ -732,43 +775,52 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fa[i]), "v"(fb[j]));
         };
         auto kstep8 = [&](int kt, bool last) {
+          const FragBase bc = frag_base(kt), bn = frag_base(kt + 1);
 #pragma unroll
           for (int p = 0; p < 64; ++p) {
-            if (p < 32 && (p & 3) == 0) {  // this stage's B4..B7, then A4..A7
-              const int f = p >> 2;
+            if (p % kCurRd8 == 0 && p / kCurRd8 < 8) {  // this stage's B4..B7, then A4..A7
+              const int f = p / kCurRd8;
               if (f < 4) {
                 keep(fb[4 + f]);
-                fb[4 + f] = read_frag8(kt, 1, 4 + f);
+                fb[4 + f] = read_frag8(bc, 1, 4 + f);
               } else {
                 keep(fa[f]);
-                fa[f] = read_frag8(kt, 0, f);
+                fa[f] = read_frag8(bc, 0, f);
               }
             }
-            if (!last && p % 3 == 1 && p / 3 < 8) issue_one(kt + 1, 1, p / 3);  // B loads of kt + 1
-            if (!last && p == 24) issue_pf(kt + 1 + kPfAhead);
+            if (!last && p >= kB0_8 && (p - kB0_8) % kLoad8 == 0 && (p - kB0_8) / kLoad8 < 8)
+              issue_one(kt + 1, 1, (p - kB0_8) / kLoad8);  // B loads of kt + 1
+            if (!last && p == kPf8At) issue_pf(kt + 1 + kPfAhead);
             if (!last && p == kBar8) {
               __builtin_amdgcn_s_waitcnt(kVmNext);  // this wave's loads of stage kt + 1 have landed
               fix_tail(kt + 1);
               __builtin_amdgcn_s_waitcnt(kLgkm0);  // and its reads of stage kt are done
               __builtin_amdgcn_s_barrier();
             }
-            if (!last && p >= kBar8 && p < kBar8 + 16 && ((p - kBar8) & 1) == 0) {  // next stage's A0..A3, B0..B3
+            if (!last && p >= kBar8 && p < kBar8 + 8 && ((p - kBar8) & 1) == 0) {  // next stage's A0..A3
               const int f = (p - kBar8) >> 1;
-              if (f < 4) {
-                keep(fa[f]);
-                fa[f] = read_frag8(kt + 1, 0, f);
-              } else {
-                keep(fb[f - 4]);
-                fb[f - 4] = read_frag8(kt + 1, 1, f - 4);
-              }
+              keep(fa[f]);
+              fa[f] = read_frag8(bn, 0, f);
             }
-            if (p > kBar8 && (p - kBar8) % 3 == 1 && (p - kBar8) / 3 < 8 && kt + 2 < nkv)
-              issue_one(kt + 2, 0, (p - kBar8) / 3);  // A loads of kt + 2
+            if (!last && p >= kNxB8 && p < kNxB8 + 8 && ((p - kNxB8) & 1) == 0) {  // and B0..B3
+              const int f = (p - kNxB8) >> 1;
+              keep(fb[f]);
+              fb[f] = read_frag8(bn, 1, f);
+            }
+            if (p > kBar8 && (p - kBar8 - 1) % kLoad8 == 0 && (p - kBar8 - 1) / kLoad8 < 8 && kt + 2 < nkv)
+              issue_one(kt + 2, 0, (p - kBar8 - 1) / kLoad8);  // A loads of kt + 2
             const int q = p >> 4, r = p & 15;
             mma8(last, ((q & 2) ? 4 : 0) + (r >> 2), ((q & 1) ? 4 : 0) + (r & 3));
             __builtin_amdgcn_sched_barrier(0);
           }
         };
+        // The zeroed accumulators are pinned here, long before the first inline MFMA that
+        // accumulates into them (left alone, the compiler sinks each zeroing to just before
+        // that MFMA, closer than the matrix core's operand wait states allow).
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
         // ---- prologue: stage 0 loaded and visible, its A0..A3 and B0..B3 read, the A
         // loads of stage 1 issued ----
 #pragma unroll
@@ -777,10 +829,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         fix_tail(0);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         __builtin_amdgcn_s_barrier();
+        {
+          const FragBase b0 = frag_base(0);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          fa[f] = read_frag8(0, 0, f);
-          fb[f] = read_frag8(0, 1, f);
+          for (int f = 0; f < 4; ++f) {
+            fa[f] = read_frag8(b0, 0, f);
+            fb[f] = read_frag8(b0, 1, f);
+          }
         }
         if (nkv > 1) {
 #pragma unroll
