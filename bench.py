@@ -165,33 +165,37 @@ def workload_label(cfg, frac, fp8=False):
 
 
 def clock_snapshot():
-    """Current and maximum engine/memory clocks and the power cap of the GPU, read with
-    rocm-smi (best effort: None fields where the tool or a field is unavailable)."""
-    import shutil
-    import subprocess
+    """Current engine and memory clock levels and the power cap of the GPU(s), read from
+    sysfs (no other program is started: this process has initialised the GPU).  None
+    where a file is missing."""
+    import glob
 
-    out = {"sclk": None, "mclk": None, "power_cap_w": None, "source": "rocm-smi"}
-    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
-    if not os.path.exists(exe):
-        out["source"] = "unavailable"
-        return out
-    try:
-        res = subprocess.run([exe, "--showclocks", "--showmaxpower", "--json"], capture_output=True,
-                             text=True, timeout=30)
-        d, _ = json.JSONDecoder().raw_decode(res.stdout[res.stdout.find("{"):])
-    except Exception as e:  # noqa: BLE001 -- reporting only
-        out["source"] = f"rocm-smi failed: {type(e).__name__}"
-        return out
-    card = d.get("card0") or next((v for k, v in d.items() if k.startswith("card")), {})
-    for k, v in card.items():
-        kl = k.lower()
-        if kl.startswith("sclk") and "speed" in kl:
-            out["sclk"] = v
-        elif kl.startswith("mclk") and "speed" in kl:
-            out["mclk"] = v
-        elif "power" in kl and ("max" in kl or "cap" in kl):
-            out["power_cap_w"] = v
-    return out
+    def cur(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return line.split(":", 1)[1].strip(" *\n")
+        except OSError:
+            return None
+        return None
+
+    cards = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        if not os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+            continue
+        cap = None
+        for hw in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_cap")):
+            try:
+                with open(hw) as f:
+                    cap = int(f.read().strip()) / 1e6
+            except (OSError, ValueError):
+                pass
+        cards.append({"card": os.path.basename(os.path.dirname(dev)), "sclk": cur(os.path.join(dev, "pp_dpm_sclk")),
+                      "mclk": cur(os.path.join(dev, "pp_dpm_mclk")), "power_cap_w": cap})
+    if not cards:
+        return {"source": "sysfs unavailable"}
+    return {"source": "sysfs", "cards": cards[:8]}
 
 
 def input_sha256(*tensors, chunk=1 << 28):
