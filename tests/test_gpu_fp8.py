@@ -173,7 +173,8 @@ def test_fp8_full_size_llama_head_spot_checks():
     """The Llama-3-8B-like head in fp8 at full T, H, V: forward outputs and d_hidden rows
     on sampled tokens against the oracle's per-token definitions (exact at any T),
     inactive rows +0, and the d_weight identities sum_v dW[v, :] = 0 and
-    <dH, h> = <dW, W> (h, W the dequantized values)."""
+    <dH, h> = <dW, W> (h, W the dequantized values).  (Written out here; the stress-head
+    check below shares the steps through _fp8_full_size_checks.)"""
     from oracle import lmhead as O
     cfg = CONFIGS[2]
     dev = cuda_device()
@@ -213,3 +214,84 @@ def test_fp8_full_size_llama_head_spot_checks():
     lhs = float((dH.double() * h_val).sum())
     rhs = float((dW64 * W_val).sum())
     assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs)), (lhs, rhs)
+
+
+def _fp8_full_size_checks(cid, frac):
+    from oracle import lmhead as O
+    cfg = CONFIGS[cid]
+    dev = cuda_device()
+    mask, _ = make_mask(cid, active_frac=frac)
+    T, H, V = cfg.T, cfg.H, cfg.V
+    announce(f"fp8 full size config {cid} T={T} H={H} V={V} active={mask.mean():.3f}")
+    hc, s_h, Wc, s_w, y = make_tensors_fp8(T, H, V, cfg.seed, device=dev)
+    a, b = make_upstream(mask)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward_fp8(hc, s_h, Wc, s_w, y)
+    dH, dW = flh_backward_fp8(hc, s_h, Wc, s_w, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                              m_dev, meta, cfg.vocab_split)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cid)
+    act = np.nonzero(mask)[0]
+    rows = np.unique(np.concatenate([[0, T - 1, 127, 128, T - 129], rng.choice(act, 96, replace=False),
+                                     rng.integers(0, T, 64)]))
+    Wf = F.dequantize(Wc.cpu().numpy(), s_w)
+    hr = F.dequantize(hc[torch.as_tensor(rows, device=dev)].cpu().numpy(), s_h)
+    yr = y.cpu().numpy()[rows]
+    olp, oent, olse = O.forward(hr, Wf, yr)
+    assert max_abs(lp.cpu().numpy()[rows], olp) <= TOL_LP
+    assert max_abs(ent.cpu().numpy()[rows], oent) <= TOL_LP
+    assert max_abs(lse.cpu().numpy()[rows], olse) <= TOL_LP
+    ar = rows[mask[rows] != 0]
+    sel = np.searchsorted(rows, ar)
+    odH = O.dhidden_rows(hr[sel], Wf, yr[sel], mask[ar], a[ar], b[ar], range(len(ar)))
+    assert rel_fro(host64(dH[torch.as_tensor(ar, device=dev)]), odH) <= TOL_GRAD
+    del Wf
+    assert not dH.view(torch.int16)[torch.as_tensor(mask == 0, device=dev)].any()
+    dW64 = dW.double()
+    col_sum, col_abs = dW64.sum(dim=0), dW64.abs().sum(dim=0)
+    assert float((col_sum.abs() / col_abs.clamp_min(1e-300)).max()) <= 1e-2
+    lhs = float((dH.double() * (hc.view(torch.float8_e4m3fn).double() * s_h)).sum())
+    rhs = float((dW64 * (Wc.view(torch.float8_e4m3fn).double() * s_w)).sum())
+    assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs)), (lhs, rhs)
+
+
+def test_fp8_full_size_stress_head_spot_checks():
+    """The stress head at 50% active in fp8 (the `bench.py --dtype fp8` workload): sampled
+    forward outputs and d_hidden rows against the oracle, inactive rows +0, d_weight
+    identities."""
+    _fp8_full_size_checks(5, 0.5)
+
+
+@pytest.mark.parametrize("cid,frac", [(4, None), (5, 0.25)])
+def test_fp8_full_hv_t_slice_against_oracle(cid, frac):
+    """1024-token slices at full H and V in fp8, every output against the oracle."""
+    cfg = CONFIGS[cid]
+    dev = cuda_device()
+    L = 1024
+    mask_full, _ = make_mask(cid, active_frac=frac)
+    c = np.concatenate([[0], np.cumsum(mask_full, dtype=np.int64)])
+    starts = np.arange(0, len(mask_full) - L + 1, 64)
+    t0 = int(starts[np.argmin(np.abs((c[starts + L] - c[starts]) / L - 0.5))])
+    mask = np.ascontiguousarray(mask_full[t0:t0 + L])
+    announce(f"fp8 T-slice config {cid} tokens [{t0}, {t0 + L}) H={cfg.H} V={cfg.V}")
+    hc_full, s_h, Wc, s_w, y_full = make_tensors_fp8(cfg.T, cfg.H, cfg.V, cfg.seed, device=dev)
+    hc = hc_full[t0:t0 + L].contiguous()
+    y = y_full[t0:t0 + L].contiguous()
+    del hc_full, y_full
+    a, b = make_upstream(mask)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward_fp8(hc, s_h, Wc, s_w, y)
+    dH, dW = flh_backward_fp8(hc, s_h, Wc, s_w, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                              m_dev, meta, cfg.vocab_split)
+    torch.cuda.synchronize()
+    hn, Wn, yn = hc.cpu().numpy(), Wc.cpu().numpy(), y.cpu().numpy()
+    olp, oent, olse = F.forward(hn, s_h, Wn, s_w, yn)
+    assert max_abs(lp.cpu().numpy(), olp) <= TOL_LP
+    assert max_abs(ent.cpu().numpy(), oent) <= TOL_LP
+    odH, odW = F.backward(hn, s_h, Wn, s_w, yn, mask, a, b)
+    gdW = host64(dW)
+    assert rel_fro(host64(dH), odH) <= TOL_GRAD
+    assert rel_fro(gdW, odW) <= TOL_GRAD and tile_rel_fro(gdW, odW) <= TOL_TILE
+    assert not dH.view(torch.int16).cpu().numpy()[mask == 0].any()

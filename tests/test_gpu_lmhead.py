@@ -288,6 +288,10 @@ def test_padded_tail_probe_matches_live_width(T, H, V, split, skip_dw):
                           padded_tail=True)
     torch.cuda.synchronize()
     assert torch.equal(live[0], padded[0]) and torch.equal(live[1], padded[1])
+    # and the padded probe's own results against the oracle
+    odH, odW = O.backward(host64(h), host64(W), y.cpu().numpy(), mask, a, b)
+    assert rel_fro(host64(padded[0]), odH) <= TOL_GRAD and rel_fro(host64(padded[1]), odW) <= TOL_GRAD
+    assert tile_rel_fro(host64(padded[1]), odW) <= TOL_TILE
 
 
 def test_padded_tail_probe_rejects_fp32():
