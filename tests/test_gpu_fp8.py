@@ -295,3 +295,47 @@ def test_fp8_full_hv_t_slice_against_oracle(cid, frac):
     assert rel_fro(host64(dH), odH) <= TOL_GRAD
     assert rel_fro(gdW, odW) <= TOL_GRAD and tile_rel_fro(gdW, odW) <= TOL_TILE
     assert not dH.view(torch.int16).cpu().numpy()[mask == 0].any()
+
+
+def test_fp8_full_size_dweight_every_entry_on_sampled_upstream():
+    """The stress head at 50% in fp8: full-size d_weight entry by entry (and tile by tile)
+    against the oracle's backward of 256 sampled tokens, the upstream gradients being zero
+    elsewhere (tokens enter the loss independently, so that is the whole d_weight);
+    d_hidden: the sampled active rows against the oracle, every other row exactly zero."""
+    cfg = CONFIGS[5]
+    dev = cuda_device()
+    mask, _ = make_mask(5, active_frac=0.5)
+    T, H, V = cfg.T, cfg.H, cfg.V
+    announce(f"fp8 full-size dW, sampled upstream: T={T} H={H} V={V}")
+    hc, s_h, Wc, s_w, y = make_tensors_fp8(T, H, V, cfg.seed, device=dev)
+    rng = np.random.default_rng(205)
+    act_all = np.nonzero(mask)[0]
+    rows = np.unique(np.concatenate([rng.choice(act_all, 240, replace=False), [act_all[0], act_all[-1]],
+                                     rng.choice(np.nonzero(mask == 0)[0], 14, replace=False)]))
+    a_full, b_full = make_upstream(mask)
+    a = np.zeros_like(a_full)
+    b = np.zeros_like(b_full)
+    a[rows], b[rows] = a_full[rows], b_full[rows]
+    off = rows[mask[rows] == 0]
+    a[off], b[off] = 0.75, -0.5  # nonzero upstream on inactive tokens: the mask must zero it
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward_fp8(hc, s_h, Wc, s_w, y)
+    dH, dW = flh_backward_fp8(hc, s_h, Wc, s_w, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                              m_dev, meta, cfg.vocab_split)
+    torch.cuda.synchronize()
+    keep = np.zeros(T, bool)
+    keep[rows[mask[rows] != 0]] = True
+    assert not bool((dH[torch.as_tensor(~keep, device=dev)] != 0).any())
+    hn = hc[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    gdH = host64(dH[torch.as_tensor(rows, device=dev)])
+    del dH, hc
+    odH, odW = F.backward(hn, s_h, Wc.cpu().numpy(), s_w, y.cpu().numpy()[rows], mask[rows], a[rows], b[rows])
+    act = mask[rows] != 0
+    assert rel_fro(gdH[act], odH[act]) <= TOL_GRAD
+    assert not gdH[~act].any()
+    gdW = host64(dW)
+    del dW
+    torch.cuda.empty_cache()
+    assert rel_fro(gdW, odW) <= TOL_GRAD
+    assert tile_rel_fro(gdW, odW) <= TOL_TILE

@@ -23,6 +23,12 @@ T-slices of configs 2-5 (1024 tokens chosen to straddle active and inactive runs
 also checked against the full oracle at full H and V, d_weight tile by tile as well.
 The long weight-gradient loop (K = T) is checked element by element at the stress
 workload's full T with small H and V, where the oracle can afford every output.
+
+Every d_weight entry at full T, H and V: tokens enter the loss independently, so with the
+upstream gradients zero outside 256 sampled tokens the full-size d_weight is exactly the
+oracle's weight gradient of those 256 tokens alone, which the oracle can afford; the kernels
+still run the whole workload (every active tile, K = T), so a lost or misplaced 256 x 256
+block of d_weight, or a wrong stage of the long contraction, shows.
 """
 
 import numpy as np
@@ -250,3 +256,66 @@ def test_long_token_axis_against_full_oracle(frac):
     den = np.linalg.norm(odH[act], axis=1)
     assert np.all(num <= 3e-2 * den + 1e-12)
     assert not dH.view(torch.int16).cpu().numpy()[mask == 0].any()
+
+
+def _sampled_upstream(mask, n, seed):
+    """Upstream gradients zero except on n sampled tokens (n - 16 active, 16 inactive, which
+    the mask must silence), the samples spread over all of T."""
+    rng = np.random.default_rng(seed)
+    act = np.nonzero(mask)[0]
+    ina = np.nonzero(mask == 0)[0]
+    pick = set(int(x) for x in rng.choice(act, size=min(len(act), n - 16), replace=False))
+    pick.update((int(act[0]), int(act[-1])))
+    if len(ina):
+        pick.update(int(x) for x in rng.choice(ina, size=min(len(ina), 16), replace=False))
+    rows = np.array(sorted(pick), dtype=np.int64)
+    a_full, b_full = make_upstream(mask)
+    a = np.zeros_like(a_full)
+    b = np.zeros_like(b_full)
+    a[rows] = a_full[rows]
+    b[rows] = b_full[rows]
+    off = rows[mask[rows] == 0]
+    a[off], b[off] = 0.75, -0.5  # nonzero upstream on inactive tokens: the mask must zero it
+    return rows, a, b
+
+
+@pytest.mark.parametrize("cid,frac", [(2, None), (4, None), (5, 0.5)])
+def test_full_size_dweight_every_entry_on_sampled_upstream(cid, frac):
+    """Full-size d_weight entry by entry (and tile by tile) against the oracle's backward of
+    256 sampled tokens, the upstream gradients being zero elsewhere; d_hidden: the sampled
+    active rows against the oracle, every other row exactly zero."""
+    cfg = CONFIGS[cid]
+    dev = cuda_device()
+    mask, _ = make_mask(cid, active_frac=frac)
+    T, H, V = cfg.T, cfg.H, cfg.V
+    announce(f"full-size dW, sampled upstream: config {cid} T={T} H={H} V={V} split={cfg.vocab_split}")
+    h, W, y = make_tensors(T, H, V, cfg.dtype, cfg.seed, device=dev)
+    rows, a, b = _sampled_upstream(mask, 256, seed=100 + cid)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward(h, W, y)
+    dH, dW = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                          m_dev, meta, cfg.vocab_split)
+    torch.cuda.synchronize()
+    # d_hidden: zero outside the sampled active rows (value zero: an active row with zero
+    # upstream sums products 0 * x)
+    keep = np.zeros(T, bool)
+    keep[rows[mask[rows] != 0]] = True
+    assert not bool((dH[torch.as_tensor(~keep, device=dev)] != 0).any())
+    hr = host64(h[torch.as_tensor(rows, device=dev)])
+    yr = y.cpu().numpy()[rows]
+    gdH = host64(dH[torch.as_tensor(rows, device=dev)])
+    del dH, h
+    Wf = host64(W)
+    del W
+    odH, odW = O.backward(hr, Wf, yr, mask[rows], a[rows], b[rows])
+    del Wf
+    act = mask[rows] != 0
+    assert rel_fro(gdH[act], odH[act]) <= TOL_GRAD
+    assert not gdH[~act].any() and not odH[~act].any()
+    gdW = host64(dW)
+    del dW
+    torch.cuda.empty_cache()
+    assert rel_fro(gdW, odW) <= TOL_GRAD, rel_fro(gdW, odW)
+    worst = tile_rel_fro(gdW, odW)
+    assert worst <= TOL_TILE, worst
