@@ -228,7 +228,7 @@ flh_status flh_forward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, fl
  *   Limit: flh_workspace_bytes(FLH_OP_FORWARD, dt, T, H, V, 0) must not exceed
  *   FLH_NOALLOC_SCRATCH_BYTES (128 MiB: for V = 128256, up to T = 16743 tokens), else
  *   FLH_E_SCRATCH and nothing is enqueued.  Other arguments and errors as for
- *   flh_forward_ex.
+ *   flh_forward_ex (bf16 and fp32 inputs; FLH_FP8_E4M3: FLH_E_UNSUPPORTED).
  *   Every call on one GPU shares that GPU's array, which keeps the last call's
  *   contents (every byte a call reads was written earlier in the same call, so nothing
  *   needs clearing): calls that may overlap on one GPU (other streams, other host

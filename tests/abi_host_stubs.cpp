@@ -37,6 +37,7 @@ hipError_t launch_finalize(int, int64_t, int64_t, const float *, const uint8_t *
 extern "C" flh_status flh_forward_noalloc(flh_dtype dt, const void *h, const void *W, const int64_t *targets,
                                           int64_t T, int64_t H, int64_t V, float *logprob, float *entropy,
                                           float *lse, const flh_active_meta *meta, void *, uint32_t flags) {
+  if (dt == FLH_FP8_E4M3) return FLH_E_UNSUPPORTED;
   const flh_status chk = flh::forward_check(dt, h, W, targets, T, H, V, logprob, entropy, lse, meta, flags);
   if (chk != FLH_OK) return chk;
   if (flh_workspace_bytes(FLH_OP_FORWARD, dt, T, H, V, 0) > FLH_NOALLOC_SCRATCH_BYTES) return FLH_E_SCRATCH;

@@ -203,6 +203,7 @@ def test_noalloc_forward_validation():
     L = lib()
     cap = 128 << 20
     assert _fwd_na(dt=4) == E["FLH_E_DTYPE"]
+    assert _fwd_na(dt=2) == E["FLH_E_UNSUPPORTED"]  # fp8 needs its scales (flh_forward_fp8)
     assert _fwd_na(h=None) == E["FLH_E_NULL"] and _fwd_na(lp=None) == E["FLH_E_NULL"]
     assert _fwd_na(H=12) == E["FLH_E_SHAPE"]
     assert _fwd_na(flags=1 << 4) == E["FLH_E_UNSUPPORTED"]
