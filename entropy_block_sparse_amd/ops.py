@@ -133,6 +133,20 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
 
 
+def _use_workspace(workspace: Optional[torch.Tensor], need: int, dev) -> Tuple[torch.Tensor, int]:
+    """(buffer, size in bytes): the caller's workspace, which must be a contiguous tensor on
+    the call's device with at least `need` bytes, or, if None, a new one."""
+    if workspace is None:
+        ws = _workspace(need, dev)
+        return ws, ws.numel()
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return workspace, nbytes
+
+
 def _check_operands(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor):
     """(T, H, V) of a call, after the checks the C ABI cannot make from plain pointers:
     the kernels would read past a tensor that is shorter than the sizes say."""
@@ -171,16 +185,16 @@ def flh_forward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     ent = torch.empty(T, dtype=torch.float32, device=dev)
     lse = torch.empty(T, dtype=torch.float32, device=dev)
     need = flh_workspace_bytes(OP_FORWARD, h.dtype, T, H, V)
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    ws, ws_bytes = _use_workspace(workspace, need, dev)
     if skip_inactive:
         if meta is None:
             raise ValueError("skip_inactive needs the active metadata (flh_spans_build)")
         check(lib().flh_forward_ex(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), T, H, V, _ptr(lp),
-                                   _ptr(ent), _ptr(lse), ctypes.byref(meta.struct), _ptr(ws), ws.numel(),
+                                   _ptr(ent), _ptr(lse), ctypes.byref(meta.struct), _ptr(ws), ws_bytes,
                                    _stream(dev), FLH_FWD_SKIP_INACTIVE), "flh_forward_ex")
     else:
         check(lib().flh_forward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), T, H, V, _ptr(lp),
-                                _ptr(ent), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev)), "flh_forward")
+                                _ptr(ent), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)), "flh_forward")
     return lp, ent, lse
 
 
@@ -219,18 +233,18 @@ def flh_backward(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: t
     need = flh_workspace_bytes(OP_BACKWARD, h.dtype, T, H, V, vocab_split)
     if need == 0:
         raise ValueError("invalid sizes or vocab_split")
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    ws, ws_bytes = _use_workspace(workspace, need, dev)
     mp = ctypes.byref(meta.struct) if meta is not None else None
     flags = (FLH_BWD_SKIP_INACTIVE_DW if skip_inactive_dw else 0) | (FLH_BWD_PADDED_TAIL if padded_tail else 0)
     if flags:
         check(lib().flh_backward_ex(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), _ptr(lse),
                                     _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V,
-                                    int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+                                    int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes,
                                     _stream(dev), flags), "flh_backward_ex")
     else:
         check(lib().flh_backward(_dtype_code(h), _ptr(h), _ptr(W), _ptr(targets), _ptr(lse),
                                  _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V,
-                                 int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+                                 int(vocab_split), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes,
                                  _stream(dev)), "flh_backward")
     return dH, dW
 
@@ -268,12 +282,12 @@ def flh_forward_fp8(h: torch.Tensor, scale_h: float, W: torch.Tensor, scale_w: f
     dev = h.device
     lp, ent, lse = (torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3))
     need = flh_workspace_bytes(OP_FORWARD, torch.uint8, T, H, V)
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    ws, ws_bytes = _use_workspace(workspace, need, dev)
     if skip_inactive and meta is None:
         raise ValueError("skip_inactive needs the active metadata (flh_spans_build)")
     mp = ctypes.byref(meta.struct) if (skip_inactive and meta is not None) else None
     check(lib().flh_forward_fp8(_ptr(h), float(scale_h), _ptr(W), float(scale_w), _ptr(targets), T, H, V,
-                                _ptr(lp), _ptr(ent), _ptr(lse), mp, _ptr(ws), ws.numel(), _stream(dev),
+                                _ptr(lp), _ptr(ent), _ptr(lse), mp, _ptr(ws), ws_bytes, _stream(dev),
                                 FLH_FWD_SKIP_INACTIVE if skip_inactive else 0), "flh_forward_fp8")
     return lp, ent, lse
 
@@ -306,11 +320,11 @@ def flh_backward_fp8(h: torch.Tensor, scale_h: float, W: torch.Tensor, scale_w: 
     need = flh_workspace_bytes(OP_BACKWARD, torch.uint8, T, H, V, vocab_split)
     if need == 0:
         raise ValueError("invalid sizes or vocab_split")
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    ws, ws_bytes = _use_workspace(workspace, need, dev)
     mp = ctypes.byref(meta.struct) if meta is not None else None
     check(lib().flh_backward_fp8(_ptr(h), float(scale_h), _ptr(W), float(scale_w), _ptr(targets), _ptr(lse),
                                  _ptr(entropy), _ptr(g_lp), _ptr(g_ent), _ptr(m), mp, T, H, V, int(vocab_split),
-                                 _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev),
+                                 _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes, _stream(dev),
                                  FLH_BWD_SKIP_INACTIVE_DW if skip_inactive_dw else 0), "flh_backward_fp8")
     return dH, dW
 

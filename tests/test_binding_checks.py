@@ -65,3 +65,20 @@ def test_cpu_tensors_are_refused_after_the_checks():
         flh_forward(h, W, y)
     with pytest.raises(ValueError, match="HIP device"):
         flh_backward(h, W, y, f, f, f, f, m, None)
+
+
+def test_workspace_argument_is_checked_in_bytes():
+    """A caller's workspace is measured in bytes (any dtype) and must be contiguous, on the
+    call's device and large enough; too small or elsewhere raises instead of allocating."""
+    from entropy_block_sparse_amd.ops import _use_workspace
+    cpu = torch.device("cpu")
+    ws, n = _use_workspace(torch.empty(100, dtype=torch.float32), 400, cpu)
+    assert n == 400 and ws.numel() == 100
+    with pytest.raises(ValueError, match="bytes"):
+        _use_workspace(torch.empty(99, dtype=torch.float32), 400, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        _use_workspace(torch.empty(200, 4, dtype=torch.uint8).t(), 400, cpu)
+    with pytest.raises(ValueError, match="device"):
+        _use_workspace(torch.empty(400, dtype=torch.uint8), 400, torch.device("meta"))
+    ws, n = _use_workspace(None, 1000, cpu)
+    assert ws.dtype == torch.uint8 and n >= 1000
