@@ -15,7 +15,11 @@ using namespace flh;
 namespace {
 
 constexpr int32_t kDefaultSplit = 16384;
-constexpr int64_t kMaxDim = (int64_t)1 << 31;  // token/vocabulary indices are int32 on device
+// T, H, V < 2^24: a wave addresses its 64 rows of an operand from one buffer base with
+// 32-bit byte offsets (row * row stride + stage offset), and the backward's transposed
+// operands (h^T, the vocabulary-major d-logits staging) have rows of about T elements,
+// so 64 rows of them stay within 2^32 bytes only for T well below 2^25.
+constexpr int64_t kMaxDim = (int64_t)1 << 24;
 
 enum KernelId : int32_t {
   kIdSpans = 0,
@@ -66,7 +70,7 @@ bool scales_ok(float scale_h, float scale_w) {
   return z >= 1e-30 && z <= 1e30;
 }
 
-// Sizes shared by both calls: T, V in [1, 2^31); H a positive multiple of one
+// Sizes shared by both calls: T, H, V in [1, 2^24); H a multiple of one
 // 16-byte chunk.
 bool dims_ok(flh_dtype dt, int64_t T, int64_t H, int64_t V) {
   const int64_t per = 16 / elt_size(dt);

@@ -38,6 +38,9 @@
  *   - Matrices are row-major and contiguous: h [T,H], W [V,H], d_hidden [T,H],
  *     d_weight [V,H].  h, W, d_hidden, d_weight must be 16-byte aligned and H a
  *     multiple of 16 bytes of elements (8 for bf16, 4 for fp32).
+ *   - T, H and V are at most 2^24 - 1 (else FLH_E_SHAPE): the kernels address a
+ *     wave's 64 operand rows from one base with 32-bit byte offsets, and the
+ *     backward's transposed operands have rows about T elements long.
  *   - Every argument is checked on the host before anything is launched; a bad
  *     argument returns an error status and enqueues nothing.  FLH_E_HIP means a
  *     launch failed (its work may be partially enqueued).  Nothing aborts and no
@@ -154,7 +157,7 @@ size_t flh_workspace_bytes(flh_op op, flh_dtype dt, int64_t T, int64_t H, int64_
  *   loss_mask  [T] uint8, nonzero = active (the RL loss mask, Bugbot "Overview").
  *   meta       host struct, see flh_active_meta; meta->T is the length of the mask.
  * Errors: FLH_E_NULL (mask, meta or a meta pointer NULL), FLH_E_SHAPE (T <= 0 or
- * T >= 2^31, tile_m <= 0), FLH_E_META (max_gap < 0 or span_cap too small).
+ * T >= 2^24, tile_m <= 0), FLH_E_META (max_gap < 0 or span_cap too small).
  */
 flh_status flh_spans_build(const uint8_t *loss_mask, flh_active_meta *meta, void *ws,
                            size_t ws_bytes, void *stream);

@@ -89,6 +89,7 @@ def test_spans_build_validation():
     assert call(FAKE, _meta(cnt=None)) == E["FLH_E_NULL"]
     assert call(FAKE, _meta(T=0, cap=0)) == E["FLH_E_SHAPE"]
     assert call(FAKE, _meta(T=1 << 31, cap=10 ** 9)) == E["FLH_E_SHAPE"]
+    assert call(FAKE, _meta(T=1 << 24, cap=10 ** 9)) == E["FLH_E_SHAPE"]
     assert call(FAKE, _meta(tm=0)) == E["FLH_E_SHAPE"]
     assert call(FAKE, _meta(G=-1, cap=100)) == E["FLH_E_META"]
     assert call(FAKE, _meta(T=1000, G=0, cap=499)) == E["FLH_E_META"]   # needs 500
@@ -106,6 +107,13 @@ def test_forward_validation():
     assert _fwd(T=0) == E["FLH_E_SHAPE"]
     assert _fwd(V=0) == E["FLH_E_SHAPE"]
     assert _fwd(T=1 << 31) == E["FLH_E_SHAPE"]
+    # 2^24: a wave's 64 rows of the backward's transposed operands (rows of about T
+    # elements) would need byte offsets past 2^32
+    for k in ("T", "H", "V"):
+        assert _fwd(**{k: 1 << 24}) == E["FLH_E_SHAPE"], k
+        assert _fwd(**{k: (1 << 24) - 8}, nbytes=100) == E["FLH_E_WORKSPACE"], k  # accepted size
+    assert lib().flh_workspace_bytes(2, 1, 1 << 24, 64, 2048, 0) == 0
+    assert lib().flh_workspace_bytes(2, 1, (1 << 24) - 8, 64, 2048, 0) > 0
     assert _fwd(H=12) == E["FLH_E_SHAPE"]            # bf16 rows must be 16-byte multiples
     assert _fwd(dt=0, H=6) == E["FLH_E_SHAPE"]
     assert _fwd(h=FAKE_ODD) == E["FLH_E_ALIGN"]
