@@ -319,3 +319,59 @@ def test_full_size_dweight_every_entry_on_sampled_upstream(cid, frac):
     assert rel_fro(gdW, odW) <= TOL_GRAD, rel_fro(gdW, odW)
     worst = tile_rel_fro(gdW, odW)
     assert worst <= TOL_TILE, worst
+
+
+def _renewal_mask(T, seed, mean_run=175):
+    """Alternating active / inactive runs of geometric length (mean `mean_run`), vectorised."""
+    rng = np.random.default_rng(seed)
+    lens = rng.geometric(1.0 / mean_run, size=2 * (T // mean_run) + 64)
+    ends = np.cumsum(lens)
+    lens = lens[:int(np.searchsorted(ends, T)) + 1]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    m = np.zeros(T, np.uint8)
+    for s, n in zip(starts[1::2], lens[1::2]):  # odd runs active, the first run inactive
+        m[s:min(T, s + n)] = 1
+    return m
+
+
+def test_largest_token_count():
+    """T = 2^24 - 128, the largest token count the library accepts (below 2^24), with small H
+    and V: the backward's transposed operands then have rows of about 2^24 elements, so a
+    wave's 64 rows reach byte offsets near 2^31.  Spans and tile bits bit-exact over all T;
+    upstream gradients zero outside 258 sampled tokens, so every d_weight entry is the
+    oracle's gradient of those tokens alone; forward outputs and d_hidden rows on the
+    sampled tokens, every other d_hidden row exactly zero."""
+    T, H, V, split = (1 << 24) - 128, 64, 2048, 512
+    dev = cuda_device()
+    announce(f"largest T: T={T} H={H} V={V} split={split}")
+    mask = _renewal_mask(T, seed=2024)
+    h, W, y = make_tensors(T, H, V, "bf16", 2025, device=dev)
+    rows, a, b = _sampled_upstream(mask, 256, seed=2026)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    lp, ent, lse = flh_forward(h, W, y)
+    dH, dW = flh_backward(h, W, y, lse, ent, torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev),
+                          m_dev, meta, split)
+    torch.cuda.synchronize()
+    assert meta.host_spans() == S.active_spans(mask, MAX_GAP)
+    assert int(meta.active_count.item()) == int(mask.sum())
+    ref_bits = S.tile_bits(mask, TILE_M)
+    assert np.array_equal(meta.tile_bits.cpu().numpy().view(np.uint32)[:len(ref_bits)], ref_bits)
+    keep = np.zeros(T, bool)
+    keep[rows[mask[rows] != 0]] = True
+    assert not bool((dH[torch.as_tensor(~keep, device=dev)] != 0).any())
+    ridx = torch.as_tensor(rows, device=dev)
+    hr, yr = host64(h[ridx]), y.cpu().numpy()[rows]
+    Wf = host64(W)
+    olp, oent, olse = O.forward(hr, Wf, yr)
+    assert max_abs(lp.cpu().numpy()[rows], olp) <= TOL_LP
+    assert max_abs(ent.cpu().numpy()[rows], oent) <= TOL_LP
+    assert max_abs(lse.cpu().numpy()[rows], olse) <= TOL_LP
+    odH, odW = O.backward(hr, Wf, yr, mask[rows], a[rows], b[rows])
+    act = mask[rows] != 0
+    assert rel_fro(host64(dH[ridx])[act], odH[act]) <= TOL_GRAD
+    gdW = host64(dW)
+    assert rel_fro(gdW, odW) <= TOL_GRAD
+    assert tile_rel_fro(gdW, odW) <= TOL_TILE
+    del h, W, dH, dW
+    torch.cuda.empty_cache()
