@@ -5,16 +5,16 @@ no host synchronisation -- so a training step can be captured once and replayed.
 graph is replayed several times with the program's own eager work and
 synchronisations in between, and every replay must reproduce the eager outputs
 bitwise (the kernels are deterministic).  Covered for the default path and for the
-forward and weight gradient over active token tiles only.
+forward and weight gradient over active token tiles only, on bf16 and on fp8 (E4M3) inputs.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from entropy_block_sparse_amd import flh_backward, flh_forward, flh_spans_build
+from entropy_block_sparse_amd import flh_backward, flh_backward_fp8, flh_forward, flh_forward_fp8, flh_spans_build
 from tests.gpu_common import announce, cuda_device
-from workloads import make_tensors, make_upstream
+from workloads import make_tensors, make_tensors_fp8, make_upstream
 
 pytestmark = pytest.mark.gpu
 
@@ -31,12 +31,16 @@ def _mask(T, seed):
     return m
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("skip", [False, True])
-def test_captured_step_replays_match_eager(skip):
+def test_captured_step_replays_match_eager(skip, dtype):
     dev = cuda_device()
     T, H, V, split = 1000, 256, 3000, 1024
-    announce(f"graph capture T={T} H={H} V={V} skip={skip}")
-    h, W, y = [x.to(dev) for x in make_tensors(T, H, V, "bf16", 41)]
+    announce(f"graph capture T={T} H={H} V={V} skip={skip} dtype={dtype}")
+    if dtype == "fp8":
+        hc, s_h, Wc, s_w, y = make_tensors_fp8(T, H, V, 41, device=dev)
+    else:
+        h, W, y = [x.to(dev) for x in make_tensors(T, H, V, "bf16", 41)]
     mask_np = _mask(T, 42)
     a, b = make_upstream(mask_np)
     m = torch.as_tensor(mask_np).to(dev)
@@ -44,8 +48,13 @@ def test_captured_step_replays_match_eager(skip):
 
     def step():
         meta = flh_spans_build(m)
-        lp, ent, lse = flh_forward(h, W, y, meta=meta, skip_inactive=skip)
-        dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, m, meta, split, skip_inactive_dw=skip)
+        if dtype == "fp8":
+            lp, ent, lse = flh_forward_fp8(hc, s_h, Wc, s_w, y, meta=meta, skip_inactive=skip)
+            dH, dW = flh_backward_fp8(hc, s_h, Wc, s_w, y, lse, ent, g_lp, g_ent, m, meta, split,
+                                      skip_inactive_dw=skip)
+        else:
+            lp, ent, lse = flh_forward(h, W, y, meta=meta, skip_inactive=skip)
+            dH, dW = flh_backward(h, W, y, lse, ent, g_lp, g_ent, m, meta, split, skip_inactive_dw=skip)
         return lp, ent, lse, dH, dW
 
     ref = [x.clone() for x in step()]
