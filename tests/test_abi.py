@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from entropy_block_sparse_amd import _lib
@@ -256,3 +257,176 @@ def test_fp8_entry_point_validation():
     assert L.flh_workspace_bytes(1, 2, 512, 256, 4096, 0) == L.flh_workspace_bytes(1, 1, 512, 256, 4096, 0)
     assert L.flh_workspace_bytes(2, 2, 512, 256, 4096, 0) == L.flh_workspace_bytes(2, 1, 512, 256, 4096, 0)
     assert L.flh_workspace_bytes(1, 2, 512, 24, 4096, 0) == 0 and L.flh_tile_m(2) == 128
+
+
+def _random_forward_case(rng):
+    """Arguments of flh_forward_ex, each drawn valid or invalid, and the status codes the
+    invalid ones map to (the call must return one of them).  An empty set means a valid
+    call, which the caller redraws: no call here may pass validation."""
+    codes = set()
+    dt = int(rng.choice([0, 1, 1, 7, 2]))
+    if dt == 7:
+        codes.add("FLH_E_DTYPE")
+    if dt == 2:
+        codes.add("FLH_E_UNSUPPORTED")           # fp8 needs flh_forward_fp8
+    flags = int(rng.choice([0, 1, 2, 1 << 5]))
+    if flags > 1:
+        codes.add("FLH_E_UNSUPPORTED")
+    ptr = {}
+    for k in ("h", "W", "y", "lp", "ent", "lse"):
+        r = rng.random()
+        if r < 0.08:
+            ptr[k] = None
+            codes.add("FLH_E_NULL")
+        elif r < 0.16 and k in ("h", "W"):
+            ptr[k] = FAKE_ODD
+            codes.add("FLH_E_ALIGN")
+        else:
+            ptr[k] = FAKE
+    T = int(rng.choice([1, 300, 4096, 0, -3, 1 << 24]))
+    V = int(rng.choice([1, 5000, 5000, 0, 1 << 24]))
+    H = int(rng.choice([64, 256, 12, 0, 1 << 24]))
+    if T <= 0 or T >= 1 << 24 or V <= 0 or V >= 1 << 24 or H <= 0 or H >= 1 << 24 or (dt == 1 and H % 8):
+        codes.add("FLH_E_SHAPE")
+    meta = None
+    if flags == 1:
+        mr = rng.random()
+        if mr < 0.15:
+            codes.add("FLH_E_META")                # skip needs metadata
+        elif mr < 0.3:
+            meta = _meta(T=max(T, 1) + 1)
+            codes.add("FLH_E_META")                # metadata of another T
+        elif mr < 0.4:
+            meta = _meta(T=max(T, 1), tm=64)
+            codes.add("FLH_E_META")                # another tile height
+        elif mr < 0.5:
+            meta = _meta(T=max(T, 1), bits=None)
+            codes.add("FLH_E_NULL")
+        else:
+            meta = _meta(T=max(T, 1))
+            if T <= 0:
+                codes.add("FLH_E_SHAPE")
+    ws, nbytes = FAKE, 1 << 40
+    wr = rng.random()
+    if wr < 0.1:
+        ws = None
+        codes.add("FLH_E_NULL")
+    elif wr < 0.2:
+        ws = ctypes.c_void_p(0x10010)
+        codes.add("FLH_E_ALIGN")
+    elif wr < 0.45:
+        nbytes = 100
+        codes.add("FLH_E_WORKSPACE")
+    args = (dt, ptr["h"], ptr["W"], ptr["y"], T, H, V, ptr["lp"], ptr["ent"], ptr["lse"],
+            ctypes.byref(meta) if meta is not None else None, ws, nbytes, None, flags)
+    return args, codes
+
+
+def test_forward_validation_randomised():
+    """Random mixes of valid and invalid arguments: every call is rejected before any
+    launch with one of the codes its invalid arguments map to (whichever the library
+    checks first), never FLH_OK or FLH_E_HIP.  Also runs under the host sanitizers."""
+    rng = np.random.default_rng(11)
+    L = lib()
+    n = 0
+    while n < 3000:
+        args, codes = _random_forward_case(rng)
+        if not codes:
+            continue
+        st = L.flh_forward_ex(*args)
+        assert st in {E[c] for c in codes}, (args, codes, st)
+        n += 1
+
+
+def _random_backward_case(rng):
+    """As _random_forward_case, for flh_backward_ex."""
+    codes = set()
+    dt = int(rng.choice([0, 1, 1, 7, 2]))
+    if dt == 7:
+        codes.add("FLH_E_DTYPE")
+    if dt == 2:
+        codes.add("FLH_E_UNSUPPORTED")
+    flags = int(rng.choice([0, 1, 2, 3, 4, 1 << 7]))
+    if flags > 3 or (flags & 2 and dt == 0):
+        codes.add("FLH_E_UNSUPPORTED")
+    ptr = {}
+    for k in ("h", "W", "y", "lse", "ent", "dH", "dW"):
+        r = rng.random()
+        if r < 0.06:
+            ptr[k] = None
+            codes.add("FLH_E_NULL")
+        elif r < 0.12 and k in ("h", "W", "dH", "dW"):
+            ptr[k] = FAKE_ODD
+            codes.add("FLH_E_ALIGN")
+        else:
+            ptr[k] = FAKE
+    glp = FAKE if rng.random() < 0.8 else None   # optional: NULL is the zero gradient
+    gent = FAKE if rng.random() < 0.7 else None
+    T = int(rng.choice([1, 300, 4096, 0, -3, 1 << 24]))
+    V = int(rng.choice([1, 5000, 5000, 0, 1 << 24]))
+    H = int(rng.choice([64, 256, 12, 0, 1 << 24]))
+    split = int(rng.choice([0, 256, 16384, 100, -256, 384]))
+    if (T <= 0 or T >= 1 << 24 or V <= 0 or V >= 1 << 24 or H <= 0 or H >= 1 << 24 or (dt == 1 and H % 8)
+            or split < 0 or split % 256):
+        codes.add("FLH_E_SHAPE")
+    mask = FAKE
+    meta = None
+    mr = rng.random()
+    if mr < 0.3:
+        meta = None                                  # dense fallback; the mask may be NULL
+        if rng.random() < 0.5:
+            mask = None
+    else:
+        Tm = max(T, 1)
+        if mr < 0.4:
+            meta = _meta(T=Tm + 1)
+            codes.add("FLH_E_META")
+        elif mr < 0.5:
+            meta = _meta(T=Tm, tm=64)
+            codes.add("FLH_E_META")
+        elif mr < 0.58:
+            meta = _meta(T=Tm, G=-1, cap=Tm)
+            codes.add("FLH_E_META")
+        elif mr < 0.66:
+            meta = _meta(T=Tm, cap=0)
+            codes.add("FLH_E_META")                # a span list that could have dropped spans
+        elif mr < 0.74:
+            meta = _meta(T=Tm, spans=None)
+            codes.add("FLH_E_NULL")
+        elif mr < 0.8:
+            meta = _meta(T=Tm)
+            mask = None
+            codes.add("FLH_E_META")                # metadata without its mask
+        else:
+            meta = _meta(T=Tm)
+            if T <= 0:
+                codes.add("FLH_E_SHAPE")
+    ws, nbytes = FAKE, 1 << 40
+    wr = rng.random()
+    if wr < 0.08:
+        ws = None
+        codes.add("FLH_E_NULL")
+    elif wr < 0.16:
+        ws = ctypes.c_void_p(0x10010)
+        codes.add("FLH_E_ALIGN")
+    elif wr < 0.4:
+        nbytes = 100
+        codes.add("FLH_E_WORKSPACE")
+    args = (dt, ptr["h"], ptr["W"], ptr["y"], ptr["lse"], ptr["ent"], glp, gent, mask,
+            ctypes.byref(meta) if meta is not None else None, T, H, V, split,
+            ptr["dH"], ptr["dW"], ws, nbytes, None, flags)
+    return args, codes
+
+
+def test_backward_validation_randomised():
+    """As test_forward_validation_randomised, for flh_backward_ex."""
+    rng = np.random.default_rng(12)
+    L = lib()
+    n = 0
+    while n < 3000:
+        args, codes = _random_backward_case(rng)
+        if not codes:
+            continue
+        st = L.flh_backward_ex(*args)
+        assert st in {E[c] for c in codes}, (args, codes, st)
+        n += 1
