@@ -259,12 +259,12 @@ def test_fp8_entry_point_validation():
     assert L.flh_workspace_bytes(1, 2, 512, 24, 4096, 0) == 0 and L.flh_tile_m(2) == 128
 
 
-def _random_forward_case(rng):
+def _random_forward_case(rng, dts=(0, 1, 1, 7, 2)):
     """Arguments of flh_forward_ex, each drawn valid or invalid, and the status codes the
     invalid ones map to (the call must return one of them).  An empty set means a valid
     call, which the caller redraws: no call here may pass validation."""
     codes = set()
-    dt = int(rng.choice([0, 1, 1, 7, 2]))
+    dt = int(rng.choice(dts))
     if dt == 7:
         codes.add("FLH_E_DTYPE")
     if dt == 2:
@@ -338,10 +338,10 @@ def test_forward_validation_randomised():
         n += 1
 
 
-def _random_backward_case(rng):
+def _random_backward_case(rng, dts=(0, 1, 1, 7, 2)):
     """As _random_forward_case, for flh_backward_ex."""
     codes = set()
-    dt = int(rng.choice([0, 1, 1, 7, 2]))
+    dt = int(rng.choice(dts))
     if dt == 7:
         codes.add("FLH_E_DTYPE")
     if dt == 2:
@@ -429,4 +429,78 @@ def test_backward_validation_randomised():
             continue
         st = L.flh_backward_ex(*args)
         assert st in {E[c] for c in codes}, (args, codes, st)
+        n += 1
+
+
+def _random_scales(rng, codes):
+    """Two fp8 scales, each drawn valid or invalid; FLH_E_SCALE is expected unless both are
+    finite and positive with a product in [1e-30, 1e30]."""
+    pool = [0.01, 1.0, 3.5e-3, 0.0, -1.0, float("inf"), float("nan"), 1e-20, 1e20]
+    sh, sw = float(rng.choice(pool)), float(rng.choice(pool))
+    ok = all(x > 0 and x <= 3.0e38 for x in (sh, sw)) and 1e-30 <= sh * sw <= 1e30
+    if not ok:
+        codes.add("FLH_E_SCALE")
+    return sh, sw
+
+
+def test_fp8_validation_randomised():
+    """flh_forward_fp8 and flh_backward_fp8 with random mixes of valid and invalid
+    arguments and scales: always rejected before any launch, with an expected code."""
+    rng = np.random.default_rng(13)
+    L = lib()
+    n = 0
+    while n < 2000:
+        (dt, h, W, y, T, H, V, lp, ent, lse, mp, ws, nb, st, fl), codes = _random_forward_case(rng, dts=(1,))
+        sh, sw = _random_scales(rng, codes)
+        if not codes:
+            continue
+        s = L.flh_forward_fp8(h, sh, W, sw, y, T, H, V, lp, ent, lse, mp, ws, nb, st, fl)
+        assert s in {E[c] for c in codes}, (codes, s)
+        n += 1
+    n = 0
+    while n < 2000:
+        a, codes = _random_backward_case(rng, dts=(1,))
+        sh, sw = _random_scales(rng, codes)
+        if not codes:
+            continue
+        s = L.flh_backward_fp8(a[1], sh, a[2], sw, *a[3:])
+        assert s in {E[c] for c in codes}, (codes, s)
+        n += 1
+
+
+def test_spans_build_validation_randomised():
+    """flh_spans_build with random mixes of valid and invalid arguments: always rejected
+    before any launch, with an expected code."""
+    rng = np.random.default_rng(14)
+    L = lib()
+    n = 0
+    while n < 2000:
+        codes = set()
+        mask = FAKE if rng.random() < 0.85 else None
+        if mask is None:
+            codes.add("FLH_E_NULL")
+        T = int(rng.choice([1, 100, 5000, 0, -7, 1 << 24]))
+        G = int(rng.choice([0, 5, 128, -1]))
+        tm = int(rng.choice([128, 128, 0, -128]))
+        ptrs = {k: (FAKE if rng.random() < 0.9 else None) for k in ("spans", "num", "bits", "cnt")}
+        if None in ptrs.values():
+            codes.add("FLH_E_NULL")
+        if T <= 0 or T >= 1 << 24 or tm <= 0:
+            codes.add("FLH_E_SHAPE")
+        if G < 0:
+            codes.add("FLH_E_META")
+            cap = 10
+        else:
+            need = (max(T, 0) + G + 1) // (G + 2)
+            cap = need if rng.random() < 0.7 else max(need - 1, -1)
+            if cap < need:
+                codes.add("FLH_E_META")            # a span list that could drop spans
+        meta = None if rng.random() < 0.05 else ActiveMeta(
+            T, G, tm, cap, *(p.value if p else None for p in (ptrs["spans"], ptrs["num"], ptrs["bits"], ptrs["cnt"])))
+        if meta is None:
+            codes = {"FLH_E_NULL"} | ({"FLH_E_NULL"} if mask is None else set())
+        if not codes:
+            continue
+        s = L.flh_spans_build(mask, ctypes.byref(meta) if meta is not None else None, None, 0, None)
+        assert s in {E[c] for c in codes}, (T, G, tm, cap, codes, s)
         n += 1
