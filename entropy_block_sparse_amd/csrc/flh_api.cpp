@@ -62,12 +62,15 @@ Prec prec_of(flh_dtype dt, float scale_h = 1.f, float scale_w = 1.f) {
   if (dt == FLH_FP8_E4M3) return Prec{2, 1, scale_h * scale_w, scale_h, scale_w};
   return Prec{dt == FLH_BF16 ? 1 : 0, dt == FLH_BF16 ? 1 : 0, 1.f, 1.f, 1.f};
 }
-// fp8 scales: finite and positive, with a product (the logit scale) in [1e-30, 1e30]
-bool scales_ok(float scale_h, float scale_w) {
+// fp8 scales: finite and positive, with a product (the logit scale) in [1e-30, 1e30] and small
+// enough that no logit can leave the fp32 range: a logit is that product times a sum of H
+// code products, each at most 448^2 in magnitude, accumulated in fp32.
+bool scales_ok(float scale_h, float scale_w, int64_t H) {
   auto fin_pos = [](float x) { return x > 0.f && x <= 3.0e38f; };
   if (!fin_pos(scale_h) || !fin_pos(scale_w)) return false;
   const double z = (double)scale_h * (double)scale_w;
-  return z >= 1e-30 && z <= 1e30;
+  if (!(z >= 1e-30 && z <= 1e30)) return false;
+  return z * 448.0 * 448.0 * (double)(H > 0 ? H : 0) < 0x1p127;
 }
 
 // Sizes shared by both calls: T, H, V in [1, 2^24); H a multiple of one
@@ -297,7 +300,7 @@ flh_status flh_forward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, fl
                            const int64_t *targets, int64_t T, int64_t H, int64_t V, float *logprob,
                            float *entropy, float *lse, const flh_active_meta *meta, void *ws, size_t ws_bytes,
                            void *stream, uint32_t flags) {
-  if (!scales_ok(scale_h, scale_w)) return FLH_E_SCALE;
+  if (!scales_ok(scale_h, scale_w, H)) return FLH_E_SCALE;
   return forward_run(prec_of(FLH_FP8_E4M3, scale_h, scale_w), FLH_FP8_E4M3, h, W, targets, T, H, V, logprob,
                      entropy, lse, meta, ws, ws_bytes, stream, flags);
 }
@@ -389,7 +392,7 @@ flh_status flh_backward_fp8(const uint8_t *h, float scale_h, const uint8_t *W, f
                             const flh_active_meta *meta, int64_t T, int64_t H, int64_t V, int32_t vocab_split,
                             void *d_hidden, void *d_weight, void *ws, size_t ws_bytes, void *stream,
                             uint32_t flags) {
-  if (!scales_ok(scale_h, scale_w)) return FLH_E_SCALE;
+  if (!scales_ok(scale_h, scale_w, H)) return FLH_E_SCALE;
   return backward_run(prec_of(FLH_FP8_E4M3, scale_h, scale_w), FLH_FP8_E4M3, h, W, targets, lse, entropy,
                       grad_logprob, grad_entropy, loss_mask, meta, T, H, V, vocab_split, d_hidden, d_weight, ws,
                       ws_bytes, stream, flags);

@@ -210,8 +210,9 @@ flh_status flh_forward_ex(flh_dtype dt, const void *h, const void *W, const int6
  * bf16 on the codes widened exactly to bf16, with scale_w and scale_h applied to their
  * fp32 results.
  *   h [T,H], W [V,H]: uint8 codes, row-major, 16-byte aligned; H a multiple of 16.
- *   scale_h, scale_w: finite and > 0, with scale_h * scale_w in [1e-30, 1e30], else
- *   FLH_E_SCALE.
+ *   scale_h, scale_w: finite and > 0, with scale_h * scale_w in [1e-30, 1e30] and
+ *   scale_h * scale_w * 448^2 * H < 2^127 (no logit, a sum of H code products of at most
+ *   448^2 each times the scales, can leave the fp32 range), else FLH_E_SCALE.
  *   Workspace: flh_workspace_bytes(op, FLH_FP8_E4M3, ...).
  * flh_forward_fp8: arguments, options (FLH_FWD_*) and outputs as flh_forward_ex.
  */

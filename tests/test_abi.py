@@ -246,6 +246,9 @@ def test_fp8_entry_point_validation():
         assert _fwd8(sh, sw) == E["FLH_E_SCALE"], (sh, sw)
         assert _bwd8(sh, sw) == E["FLH_E_SCALE"], (sh, sw)
     assert _fwd8(H=24) == E["FLH_E_SHAPE"] and _bwd8(H=24) == E["FLH_E_SHAPE"]   # H % 16
+    # a scale product that keeps every logit finite at H = 256 but not at H = 7168
+    assert _fwd8(1e15, 1e15, H=7168) == E["FLH_E_SCALE"] and _bwd8(1e15, 1e15, H=7168) == E["FLH_E_SCALE"]
+    assert _fwd8(1e15, 1e15, H=256, nbytes=100) == E["FLH_E_WORKSPACE"]
     assert _fwd8(h=None) == E["FLH_E_NULL"]
     assert _fwd8(h=FAKE_ODD) == E["FLH_E_ALIGN"]
     assert _fwd8(flags=1) == E["FLH_E_META"]
@@ -432,12 +435,14 @@ def test_backward_validation_randomised():
         n += 1
 
 
-def _random_scales(rng, codes):
+def _random_scales(rng, codes, H):
     """Two fp8 scales, each drawn valid or invalid; FLH_E_SCALE is expected unless both are
-    finite and positive with a product in [1e-30, 1e30]."""
-    pool = [0.01, 1.0, 3.5e-3, 0.0, -1.0, float("inf"), float("nan"), 1e-20, 1e20]
+    finite and positive with a product in [1e-30, 1e30] that keeps every logit (at most
+    448^2 * H code-product units) inside the fp32 range."""
+    pool = [0.01, 1.0, 3.5e-3, 0.0, -1.0, float("inf"), float("nan"), 1e-20, 1e20, 1e15, 3e12]
     sh, sw = float(rng.choice(pool)), float(rng.choice(pool))
-    ok = all(x > 0 and x <= 3.0e38 for x in (sh, sw)) and 1e-30 <= sh * sw <= 1e30
+    ok = (all(x > 0 and x <= 3.0e38 for x in (sh, sw)) and 1e-30 <= sh * sw <= 1e30
+          and sh * sw * 448.0 * 448.0 * max(H, 0) < 2.0 ** 127)
     if not ok:
         codes.add("FLH_E_SCALE")
     return sh, sw
@@ -451,7 +456,7 @@ def test_fp8_validation_randomised():
     n = 0
     while n < 2000:
         (dt, h, W, y, T, H, V, lp, ent, lse, mp, ws, nb, st, fl), codes = _random_forward_case(rng, dts=(1,))
-        sh, sw = _random_scales(rng, codes)
+        sh, sw = _random_scales(rng, codes, H)
         if not codes:
             continue
         s = L.flh_forward_fp8(h, sh, W, sw, y, T, H, V, lp, ent, lse, mp, ws, nb, st, fl)
@@ -460,7 +465,7 @@ def test_fp8_validation_randomised():
     n = 0
     while n < 2000:
         a, codes = _random_backward_case(rng, dts=(1,))
-        sh, sw = _random_scales(rng, codes)
+        sh, sw = _random_scales(rng, codes, a[11])
         if not codes:
             continue
         s = L.flh_backward_fp8(a[1], sh, a[2], sw, *a[3:])
