@@ -263,7 +263,38 @@ def test_fp8_full_size_stress_head_spot_checks():
     _fp8_full_size_checks(5, 0.5)
 
 
-@pytest.mark.parametrize("cid,frac", [(4, None), (5, 0.25)])
+def test_fp8_full_size_skip_options_match_dense():
+    """The stress head at 50% in fp8: the forward over active tiles gives the dense forward's
+    outputs bitwise on active tiles and 0 elsewhere, and the weight gradient over active
+    tiles the dense mode's d_hidden and d_weight bitwise."""
+    cfg = CONFIGS[5]
+    dev = cuda_device()
+    mask, _ = make_mask(5, active_frac=0.5)
+    T, H, V = cfg.T, cfg.H, cfg.V
+    announce(f"fp8 full size skip options T={T} H={H} V={V}")
+    hc, s_h, Wc, s_w, y = make_tensors_fp8(T, H, V, cfg.seed, device=dev)
+    a, b = make_upstream(mask)
+    g_lp, g_ent = torch.as_tensor(a).to(dev), torch.as_tensor(b).to(dev)
+    m_dev = torch.as_tensor(mask).to(dev)
+    meta = flh_spans_build(m_dev)
+    dense = flh_forward_fp8(hc, s_h, Wc, s_w, y)
+    sparse = flh_forward_fp8(hc, s_h, Wc, s_w, y, meta=meta, skip_inactive=True)
+    torch.cuda.synchronize()
+    tiles = np.zeros(-(-T // 128), bool)
+    tiles[np.nonzero(mask)[0] // 128] = True
+    act = torch.as_tensor(np.repeat(tiles, 128)[:T]).to(dev)
+    for d, sp in zip(dense, sparse):
+        assert torch.equal(d[act], sp[act]) and not sp[~act].any()
+    lp, ent, lse = dense
+    del sparse
+    dH, dW = flh_backward_fp8(hc, s_h, Wc, s_w, y, lse, ent, g_lp, g_ent, m_dev, meta, cfg.vocab_split)
+    dH2, dW2 = flh_backward_fp8(hc, s_h, Wc, s_w, y, lse, ent, g_lp, g_ent, m_dev, meta, cfg.vocab_split,
+                                skip_inactive_dw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dH, dH2) and torch.equal(dW, dW2)
+
+
+@pytest.mark.parametrize("cid,frac", [(2, None), (3, None), (4, None), (5, 0.25)])
 def test_fp8_full_hv_t_slice_against_oracle(cid, frac):
     """1024-token slices at full H and V in fp8, every output against the oracle."""
     cfg = CONFIGS[cid]
